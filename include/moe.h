@@ -1,0 +1,227 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse mixture-of-experts layer library.
+ *
+ * One MoE layer on one device's share of T tokens: router logits, softmax
+ * top-k expert selection, per-expert token counting and index generation,
+ * token permutation into expert-contiguous order, a grouped GEMM over all
+ * experts with a SwiGLU activation between the two expert projections, the
+ * weighted un-permute (combine), and the backward pass of every step.
+ *
+ * Sources, cited by page title and section:
+ *   [Brief]   llm-wiki paper brief of arXiv 2604.00785 ("在 Aurora 超级计算机上
+ *             实现大规模 MoE 语言模型的可扩展预训练").
+ *   [Summary] shd-paper.top summary "Scalable Pretraining of Large Mixture of
+ *             Experts Language Models on Aurora Super Computer".
+ * The pages name the steps (expert selection; GPU kernels for token counting
+ * and index generation; one grouped GEMM merging every expert's products;
+ * optimised matmul and activation; forward plus backward) without formal
+ * definitions.  The definitions used here: softmax gate over all E experts,
+ * selection of the k largest logits (ties to the lower expert index), combine
+ * weights = the selected probabilities (optionally renormalised), dropless
+ * routing, stable token-major order inside each expert's group, expert FFN
+ * SwiGLU with the gate in the first F columns of W1 and the up projection in
+ * the last F.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named as tensors are DEVICE pointers owned by the caller.  The
+ *   library never allocates, frees or synchronises; every call enqueues work
+ *   on `stream` (a hipStream_t; NULL = the null stream) and returns.
+ * - Tensors are dense row-major.  Index type is int32 (T*k < 2^31).
+ * - moe_dtype selects the storage of activations and weights: MOE_F32 or
+ *   MOE_BF16.  Router logits, probabilities, gate weights and their
+ *   gradients are always float32 unless a dtype argument says otherwise.
+ *   All products accumulate in float32.
+ * - Errors: every call returns moe_status.  Validation is host-side only and
+ *   never reads device memory; on error nothing is enqueued and
+ *   moe_last_error() returns a message (thread-local, valid until the next
+ *   call on the same thread).  MOE_ERR_HIP reports a failed kernel launch.
+ *   Out-of-range expert ids or row indices inside device buffers are caller
+ *   bugs and give undefined results.
+ * - Weight layouts: router wr[d, E]; expert W1[E, d, 2F] (columns [0, F) gate,
+ *   [F, 2F) up); expert W2[E, F, d].
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, k > E, ...  */
+  MOE_ERR_UNSUPPORTED = 2, /* dtype or shape outside what the kernels take  */
+  MOE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required   */
+  MOE_ERR_HIP = 4          /* a HIP launch failed                           */
+} moe_status;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef void* moe_stream_t; /* hipStream_t */
+
+/* Maximum sizes accepted by the routing kernels. */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 32
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Library version string. */
+const char* moe_version(void);
+
+/*
+ * moe_route_topk -- expert selection [Summary, Method details / technical
+ * framework: the forward pass selects experts, then computes them].
+ *
+ * Per token t: z[t, e] = logits[t, e] + bias[e] (float32 add; bias may be
+ * NULL), p = softmax(z[t, :]) over all E experts.  Without forced_idx, slot j
+ * receives the expert with the j-th largest z (equal values: lower expert
+ * index first).  With forced_idx ([T, k] int32, k distinct ids in [0, E) per
+ * token) the ids are copied as given (forced uniform routing, [Brief,
+ * Limitations]).  topk_w[t, j] = p[t, topk_idx[t, j]], divided by
+ * sum_j p[t, topk_idx[t, j]] when renorm != 0.
+ *   logits   [T, E] float32, in.        bias [E] float32 or NULL, in.
+ *   topk_idx [T, k] int32, out.         topk_w [T, k] float32, out.
+ *   probs    [T, E] float32 or NULL, out (p, kept for the backward pass).
+ * Requires 1 <= k <= min(E, 32), 1 <= E <= 1024, T >= 1.
+ */
+moe_status moe_route_topk(const float* logits, const float* bias, int T, int E,
+                          int k, int renorm, const int32_t* forced_idx,
+                          int32_t* topk_idx, float* topk_w, float* probs,
+                          moe_stream_t stream);
+
+/*
+ * moe_route_topk_bwd -- gradient of the routing weights with respect to the
+ * logits [Brief, Key results: the sped-up unit is forward plus backward].
+ *
+ * dp[t, e] = dw[t, j] if e == topk_idx[t, j] else 0 (with renorm:
+ * dp_j = (dw_j - sum_l dw_l w_l) / S, S = sum_j p_j);
+ * dlogits[t, e] = p[t, e] * (dp[t, e] - sum_e' p[t, e'] dp[t, e']).
+ *   probs [T, E] float32, in (from moe_route_topk).
+ *   topk_idx [T, k] int32, in.          dtopk_w [T, k] float32, in.
+ *   dlogits [T, E] out, stored as dlogits_dtype (float32 or bf16).
+ */
+moe_status moe_route_topk_bwd(const float* probs, const int32_t* topk_idx,
+                              const float* dtopk_w, int T, int E, int k,
+                              int renorm, void* dlogits, moe_dtype dlogits_dtype,
+                              moe_stream_t stream);
+
+/*
+ * moe_count_index -- token counting and index generation [Brief, Core
+ * method: GPU kernels count the tokens of each expert and generate the
+ * indices that feed the grouped GEMM].
+ *
+ * Flat slot s = t*k + j has expert topk_idx[s].
+ *   counts[e]   = number of slots with expert e                 (int32 [E])
+ *   offsets[e]  = sum_{e' < e} counts[e'], offsets[E] = T*k      (int32 [E+1])
+ *   src[p]      = slot held by row p of the expert-sorted order; inside an
+ *                 expert's rows [offsets[e], offsets[e+1]) slots increase
+ *                 (stable order)                                  (int32 [T*k])
+ *   dest[s]     = row of slot s (inverse of src)                 (int32 [T*k])
+ * Deterministic: built from scans, not from atomically claimed slots.
+ * ws: device workspace of at least moe_count_index_workspace_size(T, k, E)
+ * bytes, 16-byte aligned.
+ */
+size_t moe_count_index_workspace_size(int T, int k, int E);
+moe_status moe_count_index(const int32_t* topk_idx, int T, int k, int E,
+                           int32_t* counts, int32_t* offsets, int32_t* dest,
+                           int32_t* src, void* ws, size_t ws_bytes,
+                           moe_stream_t stream);
+
+/*
+ * moe_permute -- gather token rows into expert-contiguous order:
+ * xp[p, :] = x[src[p] / k, :].  The expert computation on the pages runs on
+ * tokens grouped per expert [Brief, Core method].
+ *   x [T, d], xp [T*k, d], both `dtype`.   src [T*k] int32 from
+ *   moe_count_index.  Requires d % 8 == 0.  Bitwise copy.
+ */
+moe_status moe_permute(const void* x, const int32_t* src, int T, int k, int d,
+                       moe_dtype dtype, void* xp, moe_stream_t stream);
+
+/*
+ * moe_unpermute -- weighted combine back to token order:
+ * y[t, :] = sum_{j<k} w[t, j] * yp[dest[t*k + j], :], summed in float32 in
+ * increasing j, rounded once to `dtype`.  With w == NULL every weight is 1
+ * (this is also the backward pass of moe_permute).
+ *   yp [T*k, d], y [T, d], both `dtype`.  w [T, k] float32 or NULL.
+ *   Requires d % 8 == 0.
+ */
+moe_status moe_unpermute(const void* yp, const int32_t* dest, const float* w,
+                         int T, int k, int d, moe_dtype dtype, void* y,
+                         moe_stream_t stream);
+
+/*
+ * moe_unpermute_bwd -- backward of moe_unpermute:
+ * dyp[dest[t*k+j], :] = w[t, j] * dy[t, :]   (rounded to dtype) and
+ * dw[t, j] = sum_i dy[t, i] * yp[dest[t*k+j], i]   (float32).
+ *   dy [T, d], yp [T*k, d], dyp [T*k, d]: `dtype`.  w [T, k] float32, in.
+ *   dw [T, k] float32, out.  Requires d % 8 == 0.
+ */
+moe_status moe_unpermute_bwd(const void* dy, const void* yp,
+                             const int32_t* dest, const float* w, int T, int k,
+                             int d, moe_dtype dtype, void* dyp, float* dw,
+                             moe_stream_t stream);
+
+/*
+ * Grouped GEMM -- one launch computes every expert's product [Brief, Core
+ * method: the experts' matrix products are merged into a grouped GEMM;
+ * Summary, Method details / key design: optimised matrix multiplication].
+ *
+ * Rows [offsets[e], offsets[e+1]) of the row-major operands belong to group
+ * e; `offsets` (int32 [E+1], offsets[0] = 0, non-decreasing,
+ * offsets[E] <= M) is read ON THE DEVICE, so no host synchronisation is
+ * needed between counting and the GEMM.  M is the host-known row count.
+ *
+ * moe_grouped_gemm_fwd:  c[rows e] = a[rows e] @ b[e]
+ *   a [M, K] ab_dtype, b [E, K, N] ab_dtype, c [M, N] c_dtype.
+ *   With ab_dtype == MOE_BF16, c_dtype may be MOE_BF16 or MOE_F32;
+ *   with MOE_F32 inputs c_dtype must be MOE_F32.
+ *   Rows outside every group are left untouched.
+ *
+ * moe_grouped_gemm_bwd: given dc = dL/dc,
+ *   da[rows e] = dc[rows e] @ b[e]^T (+ da_add[rows e])   [M, K], dtype
+ *   db[e]      = a[rows e]^T @ dc[rows e]                  [E, K, N] float32
+ *   (db[e] = 0 for an empty group).  a, b, dc, da, da_add share `dtype`;
+ *   da or db may be NULL to skip that product; da_add may be NULL.
+ *
+ * The bf16 path runs on MFMA tiles when K % 8 == 0 and N % 8 == 0; other
+ * shapes and float32 run on a tiled FMA kernel.  ws/ws_bytes: reserved
+ * workspace (moe_grouped_gemm_workspace_size() bytes; currently 0, NULL ok).
+ */
+size_t moe_grouped_gemm_workspace_size(int M, int K, int N, int E,
+                                       moe_dtype dtype);
+moe_status moe_grouped_gemm_fwd(const void* a, const void* b,
+                                const int32_t* offsets, int M, int K, int N,
+                                int E, moe_dtype ab_dtype, void* c,
+                                moe_dtype c_dtype, void* ws, size_t ws_bytes,
+                                moe_stream_t stream);
+moe_status moe_grouped_gemm_bwd(const void* a, const void* b, const void* dc,
+                                const int32_t* offsets, int M, int K, int N,
+                                int E, moe_dtype dtype, void* da,
+                                const void* da_add, float* db, void* ws,
+                                size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * moe_act_fwd -- SwiGLU activation [Summary, Method details / key design:
+ * optimised activation]: a[m, f] = silu(h[m, f]) * h[m, F + f],
+ * silu(z) = z / (1 + exp(-z)).   h [M, 2F], a [M, F], both `dtype`.
+ * Requires F % 8 == 0.
+ *
+ * moe_act_bwd -- its gradient: with g = h[m, f], u = h[m, F+f],
+ * s = sigmoid(g):  dh[m, f] = da * u * s * (1 + g (1 - s)),
+ * dh[m, F+f] = da * g * s.   h, dh [M, 2F], da [M, F], all `dtype`.
+ */
+moe_status moe_act_fwd(const void* h, int M, int F, moe_dtype dtype, void* a,
+                       moe_stream_t stream);
+moe_status moe_act_bwd(const void* h, const void* da, int M, int F,
+                       moe_dtype dtype, void* dh, moe_stream_t stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,154 @@
+// SwiGLU activation between the two expert projections, and its gradient
+// [Summary, Method details / key design: optimised activation function].
+//
+// h[m, :] = [G | U] (gate columns [0, F), up columns [F, 2F));
+// a = silu(G) * U, silu(z) = z * sigmoid(z).  Elementwise and HBM-bound:
+// each thread handles one 16-byte chunk of G and the matching chunk of U.
+#include <math.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kActBlock = 256;
+
+struct alignas(16) V16 {
+  uint32_t w[4];
+};
+
+template <typename T>
+struct Elems {
+  static constexpr int N = 16 / sizeof(T);
+};
+
+template <typename T>
+__device__ __forceinline__ void load_f32(const T* p, float* f) {
+  const V16 v = *reinterpret_cast<const V16*>(p);
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = lo_bf16(v.w[i]);
+      f[2 * i + 1] = hi_bf16(v.w[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v.w[i]);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_f32(T* p, const float* f) {
+  V16 v;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v.w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v.w[i] = __float_as_uint(f[i]);
+  }
+  *reinterpret_cast<V16*>(p) = v;
+}
+
+__device__ __forceinline__ float sigmoidf_(float z) { return 1.f / (1.f + expf(-z)); }
+
+template <typename T>
+__global__ __launch_bounds__(kActBlock) void act_fwd_kernel(const T* __restrict__ h, long long M,
+                                                            int F, T* __restrict__ a) {
+  constexpr int N = Elems<T>::N;
+  const int cpr = F / N;
+  const long long total = M * cpr;
+  for (long long i = blockIdx.x * static_cast<long long>(kActBlock) + threadIdx.x; i < total;
+       i += static_cast<long long>(gridDim.x) * kActBlock) {
+    const long long m = i / cpr;
+    const int c = static_cast<int>(i - m * cpr);
+    const T* hr = h + m * 2 * F;
+    float g[N], u[N], o[N];
+    load_f32(hr + c * N, g);
+    load_f32(hr + F + c * N, u);
+#pragma unroll
+    for (int q = 0; q < N; ++q) o[q] = g[q] * sigmoidf_(g[q]) * u[q];
+    store_f32(a + m * F + c * N, o);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kActBlock) void act_bwd_kernel(const T* __restrict__ h,
+                                                            const T* __restrict__ da, long long M,
+                                                            int F, T* __restrict__ dh) {
+  constexpr int N = Elems<T>::N;
+  const int cpr = F / N;
+  const long long total = M * cpr;
+  for (long long i = blockIdx.x * static_cast<long long>(kActBlock) + threadIdx.x; i < total;
+       i += static_cast<long long>(gridDim.x) * kActBlock) {
+    const long long m = i / cpr;
+    const int c = static_cast<int>(i - m * cpr);
+    const T* hr = h + m * 2 * F;
+    float g[N], u[N], d[N], dg[N], du[N];
+    load_f32(hr + c * N, g);
+    load_f32(hr + F + c * N, u);
+    load_f32(da + m * F + c * N, d);
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      const float s = sigmoidf_(g[q]);
+      dg[q] = d[q] * u[q] * s * (1.f + g[q] * (1.f - s));
+      du[q] = d[q] * g[q] * s;
+    }
+    T* dr = dh + m * 2 * F;
+    store_f32(dr + c * N, dg);
+    store_f32(dr + F + c * N, du);
+  }
+}
+
+int act_grid(long long items) {
+  long long b = (items + kActBlock - 1) / kActBlock;
+  if (b > 256LL * 32) b = 256LL * 32;
+  return static_cast<int>(b < 1 ? 1 : b);
+}
+
+moe_status check_act(int M, int F, moe_dtype dt) {
+  MOE_REQUIRE(M >= 1 && F >= 1, MOE_ERR_INVALID_ARG, "M and F must be >= 1");
+  MOE_REQUIRE(dtype_ok(dt), MOE_ERR_UNSUPPORTED, "unknown dtype");
+  MOE_REQUIRE(F % 8 == 0, MOE_ERR_UNSUPPORTED, "F must be a multiple of 8");
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" moe_status moe_act_fwd(const void* h, int M, int F, moe_dtype dtype, void* a,
+                                  moe_stream_t stream) {
+  clear_error();
+  if (moe_status s = check_act(M, F, dtype)) return s;
+  MOE_REQUIRE(h && a, MOE_ERR_INVALID_ARG, "moe_act_fwd: null pointer");
+  const long long items = static_cast<long long>(M) * F * static_cast<long long>(dtype_size(dtype)) / 16;
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(act_fwd_kernel<uint16_t>, dim3(act_grid(items)), dim3(kActBlock), 0,
+                       as_stream(stream), static_cast<const uint16_t*>(h), (long long)M, F,
+                       static_cast<uint16_t*>(a));
+  else
+    hipLaunchKernelGGL(act_fwd_kernel<float>, dim3(act_grid(items)), dim3(kActBlock), 0,
+                       as_stream(stream), static_cast<const float*>(h), (long long)M, F,
+                       static_cast<float*>(a));
+  return check_launch("moe_act_fwd");
+}
+
+extern "C" moe_status moe_act_bwd(const void* h, const void* da, int M, int F, moe_dtype dtype,
+                                  void* dh, moe_stream_t stream) {
+  clear_error();
+  if (moe_status s = check_act(M, F, dtype)) return s;
+  MOE_REQUIRE(h && da && dh, MOE_ERR_INVALID_ARG, "moe_act_bwd: null pointer");
+  const long long items = static_cast<long long>(M) * F * static_cast<long long>(dtype_size(dtype)) / 16;
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(act_bwd_kernel<uint16_t>, dim3(act_grid(items)), dim3(kActBlock), 0,
+                       as_stream(stream), static_cast<const uint16_t*>(h),
+                       static_cast<const uint16_t*>(da), (long long)M, F,
+                       static_cast<uint16_t*>(dh));
+  else
+    hipLaunchKernelGGL(act_bwd_kernel<float>, dim3(act_grid(items)), dim3(kActBlock), 0,
+                       as_stream(stream), static_cast<const float*>(h),
+                       static_cast<const float*>(da), (long long)M, F, static_cast<float*>(dh));
+  return check_launch("moe_act_bwd");
+}

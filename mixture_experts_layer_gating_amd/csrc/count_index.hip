@@ -1,0 +1,208 @@
+// Token counting and index generation [Brief, Core method: dedicated GPU
+// kernels count each expert's tokens and generate the indices that feed the
+// grouped GEMM].
+//
+// Output (flat slot s = t*k + j, expert topk_idx[s]):
+//   counts[e], offsets[e] (exclusive scan, offsets[E] = T*k),
+//   dest[s] = row of slot s in expert-sorted order, src = inverse of dest.
+// Inside an expert's rows the slots keep increasing s (a stable sort), which
+// makes the result unique and deterministic.  No global atomics are used;
+// ranks come from wavefront ballots and LDS-staged scans.
+//
+// Three launches:
+//   1. count:   block b histograms its chunk of slots in LDS
+//               -> blk_cnt[e][b]                                  (workspace)
+//   2. scan:    one block: totals -> counts, offsets; per expert an exclusive
+//               scan over blocks -> blk_off[e][b] = first row of block b's
+//               slots of expert e
+//   3. scatter: block b re-reads its chunk; each wave ranks its slots with a
+//               64-lane match mask (one ballot per expert-id bit), adds the
+//               running per-(wave, expert) count and the block offset, and
+//               writes dest and src.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kCiBlock = 256;                 // 4 waves
+constexpr int kCiWaves = kCiBlock / kWave;
+constexpr int kCiChunk = 4096;                // slots per block
+constexpr int kCiSub = kCiChunk / kCiWaves;   // slots per wave
+constexpr int kScanBlock = 1024;
+
+inline int num_chunks(long long Tk) { return static_cast<int>((Tk + kCiChunk - 1) / kCiChunk); }
+
+__global__ __launch_bounds__(kCiBlock) void ci_count_kernel(const int32_t* __restrict__ ids,
+                                                            int Tk, int E, int nblk,
+                                                            int32_t* __restrict__ blk_cnt) {
+  extern __shared__ int32_t hist[];  // [E]
+  for (int e = threadIdx.x; e < E; e += kCiBlock) hist[e] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * kCiChunk;
+  const int end = min(base + kCiChunk, Tk);
+  for (int s = base + threadIdx.x; s < end; s += kCiBlock) atomicAdd(&hist[ids[s]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kCiBlock)
+    blk_cnt[static_cast<size_t>(e) * nblk + blockIdx.x] = hist[e];
+}
+
+__global__ __launch_bounds__(kScanBlock) void ci_scan_kernel(const int32_t* __restrict__ blk_cnt,
+                                                             int E, int nblk,
+                                                             int32_t* __restrict__ blk_off,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets) {
+  __shared__ int32_t wave_tot[kScanBlock / kWave];
+  __shared__ int32_t carry_s;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  if (threadIdx.x == 0) carry_s = 0;
+  __syncthreads();
+  // E <= 1024 = block size: one expert per thread, processed in one pass.
+  for (int e0 = 0; e0 < E; e0 += kScanBlock) {
+    const int e = e0 + threadIdx.x;
+    int tot = 0;
+    if (e < E) {
+      const int32_t* row = blk_cnt + static_cast<size_t>(e) * nblk;
+      for (int b = 0; b < nblk; ++b) tot += row[b];
+    }
+    const int inc = wave_inclusive_scan(tot, lane);
+    if (lane == kWave - 1) wave_tot[wid] = inc;
+    __syncthreads();
+    int wprefix = 0;
+    for (int w = 0; w < wid; ++w) wprefix += wave_tot[w];
+    const int carry = carry_s;
+    const int excl = carry + wprefix + inc - tot;
+    if (e < E) {
+      counts[e] = tot;
+      offsets[e] = excl;
+      const int32_t* row = blk_cnt + static_cast<size_t>(e) * nblk;
+      int32_t* orow = blk_off + static_cast<size_t>(e) * nblk;
+      int run = excl;
+      for (int b = 0; b < nblk; ++b) {
+        orow[b] = run;
+        run += row[b];
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x == kScanBlock - 1) carry_s = excl + tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) offsets[E] = carry_s;
+}
+
+// Lanes of the wave whose id equals this lane's id (only among lanes with
+// valid == true).  One ballot per id bit.
+__device__ __forceinline__ uint64_t match_mask(int id, bool valid, int nbits) {
+  uint64_t m = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (id >> b) & 1;
+    const uint64_t ones = __ballot(valid && bit);
+    m &= bit ? ones : ~ones;
+  }
+  return valid ? m : 0ull;
+}
+
+__global__ __launch_bounds__(kCiBlock) void ci_scatter_kernel(
+    const int32_t* __restrict__ ids, int Tk, int E, int nbits, int nblk,
+    const int32_t* __restrict__ blk_off, int32_t* __restrict__ dest, int32_t* __restrict__ src) {
+  extern __shared__ int32_t run[];  // [kCiWaves][E]
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  for (int i = threadIdx.x; i < kCiWaves * E; i += kCiBlock) run[i] = 0;
+  __syncthreads();
+  const int wbase = blockIdx.x * kCiChunk + wid * kCiSub;
+  const int wend = min(wbase + kCiSub, Tk);
+  int32_t* myrun = run + wid * E;
+  const uint64_t lt = lanemask_lt(lane);
+
+  // Pass 1: per-(wave, expert) counts of this block's chunk.
+  for (int s0 = wbase; s0 < wend; s0 += kWave) {
+    const int s = s0 + lane;
+    const bool valid = s < wend;
+    const int id = valid ? ids[s] : 0;
+    const uint64_t m = match_mask(id, valid, nbits);
+    if (valid && (m & lt) == 0) myrun[id] += __popcll(m);
+  }
+  __syncthreads();
+  // Exclusive scan over waves, seeded with the block's first row per expert.
+  for (int e = threadIdx.x; e < E; e += kCiBlock) {
+    int acc = blk_off[static_cast<size_t>(e) * nblk + blockIdx.x];
+    for (int w = 0; w < kCiWaves; ++w) {
+      const int c = run[w * E + e];
+      run[w * E + e] = acc;
+      acc += c;
+    }
+  }
+  __syncthreads();
+  // Pass 2: final rows.
+  for (int s0 = wbase; s0 < wend; s0 += kWave) {
+    const int s = s0 + lane;
+    const bool valid = s < wend;
+    const int id = valid ? ids[s] : 0;
+    const uint64_t m = match_mask(id, valid, nbits);
+    int row = 0;
+    if (valid) row = myrun[id] + __popcll(m & lt);
+    // All lanes have read the running count before the leader advances it.
+    __builtin_amdgcn_wave_barrier();
+    if (valid && (m & lt) == 0) myrun[id] += __popcll(m);
+    if (valid) {
+      dest[s] = row;
+      src[row] = s;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+int id_bits(int E) {
+  int b = 0;
+  while ((1 << b) < E) ++b;
+  return b;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_count_index_workspace_size(int T, int k, int E) {
+  if (T < 1 || k < 1 || E < 1) return 0;
+  const long long Tk = static_cast<long long>(T) * k;
+  const size_t nblk = static_cast<size_t>(num_chunks(Tk));
+  // blk_cnt and blk_off, each [E][nblk] int32, 256-byte aligned halves.
+  const size_t half = ((static_cast<size_t>(E) * nblk * 4 + 255) / 256) * 256;
+  return 2 * half;
+}
+
+extern "C" moe_status moe_count_index(const int32_t* topk_idx, int T, int k, int E,
+                                      int32_t* counts, int32_t* offsets, int32_t* dest,
+                                      int32_t* src, void* ws, size_t ws_bytes,
+                                      moe_stream_t stream) {
+  clear_error();
+  MOE_REQUIRE(T >= 1 && k >= 1 && E >= 1, MOE_ERR_INVALID_ARG,
+              "moe_count_index: T, k, E must be >= 1");
+  MOE_REQUIRE(k <= E, MOE_ERR_INVALID_ARG, "moe_count_index: need k <= E");
+  MOE_REQUIRE(E <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED, "moe_count_index: E exceeds 1024");
+  const long long Tk = static_cast<long long>(T) * k;
+  MOE_REQUIRE(Tk < (1ll << 31), MOE_ERR_UNSUPPORTED, "moe_count_index: T*k must be < 2^31");
+  MOE_REQUIRE(topk_idx && counts && offsets && dest && src, MOE_ERR_INVALID_ARG,
+              "moe_count_index: null pointer");
+  const size_t need = moe_count_index_workspace_size(T, k, E);
+  MOE_REQUIRE(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE,
+              "moe_count_index: workspace too small");
+  MOE_REQUIRE((reinterpret_cast<uintptr_t>(ws) & 15) == 0, MOE_ERR_WORKSPACE,
+              "moe_count_index: workspace must be 16-byte aligned");
+  const int nblk = num_chunks(Tk);
+  int32_t* blk_cnt = static_cast<int32_t*>(ws);
+  int32_t* blk_off = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + need / 2);
+  hipStream_t st = as_stream(stream);
+  hipLaunchKernelGGL(ci_count_kernel, dim3(nblk), dim3(kCiBlock), E * sizeof(int32_t), st,
+                     topk_idx, static_cast<int>(Tk), E, nblk, blk_cnt);
+  if (moe_status s = check_launch("moe_count_index/count")) return s;
+  hipLaunchKernelGGL(ci_scan_kernel, dim3(1), dim3(kScanBlock), 0, st, blk_cnt, E, nblk, blk_off,
+                     counts, offsets);
+  if (moe_status s = check_launch("moe_count_index/scan")) return s;
+  hipLaunchKernelGGL(ci_scatter_kernel, dim3(nblk), dim3(kCiBlock),
+                     kCiWaves * E * sizeof(int32_t), st, topk_idx, static_cast<int>(Tk), E,
+                     id_bits(E), nblk, blk_off, dest, src);
+  return check_launch("moe_count_index/scatter");
+}

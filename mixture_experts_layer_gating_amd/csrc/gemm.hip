@@ -1,0 +1,685 @@
+// Grouped GEMM over all experts in one launch [Brief, Core method: the
+// experts' matrix products are merged into a grouped GEMM; Summary, Method
+// details / key design: optimised matrix multiplication].
+//
+// Rows [offsets[e], offsets[e+1]) of the token-major operands belong to
+// expert e.  `offsets` is read on the device: each workgroup derives its
+// (expert, row tile, column tile) from it, so the host never waits for the
+// routing result.  Three operand layouts cover the forward and backward
+// passes (b = per-expert weights [E, K, N]):
+//
+//   NN  c[rows e]  = a[rows e]  @ b[e]          forward (reduction over K)
+//   NT  da[rows e] = dc[rows e] @ b[e]^T        input gradient (over N)
+//   TN  db[e]      = a[rows e]^T @ dc[rows e]   weight gradient (over rows)
+//
+// bf16 path: v_mfma_f32_32x32x16_bf16 (gfx950) on BMxBNx64 tiles, 4 waves in
+// a 2x2 grid, each wave (BM/2)x(BN/2).  Operand tiles are staged through LDS
+// in a k-contiguous layout, double-buffered (global loads of step k+1 are in
+// flight while the MFMAs of step k run), with the 16-byte chunk index XORed
+// with (row % 8) so that both the LDS writes and the MFMA fragment reads are
+// bank-conflict free.  An operand whose reduction index is not contiguous in
+// memory (b in NN; a and dc in TN) is loaded as 8x8 blocks and transposed in
+// registers before the LDS write.  Workgroup ids are remapped so that each
+// of the 8 XCDs (own L2) walks a contiguous range of tiles, which keeps one
+// expert's weights and rows in one L2.
+//
+// Float32 (and shapes whose K or N is not a multiple of 8) run on a plain
+// LDS-tiled FMA kernel with the same tile resolution.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+enum Mode { kNN = 0, kNT = 1, kTN = 2 };
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+struct GemmArgs {
+  const void* x;    // NN: a [M,K]   NT: dc [M,N]  TN: a [M,K]
+  const void* y;    // NN: b [E,K,N] NT: b [E,K,N] TN: dc [M,N]
+  const void* add;  // NT: optional addend [M,K]
+  void* out;        // NN: c [M,N]   NT: da [M,K]  TN: db [E,K,N] or split partials
+  const int32_t* offsets;
+  int M, K, N, E;
+  int ntm;    // TN: row tiles over K
+  int ntn;    // column tiles
+  int split;  // TN: reduction slices (partials written to out as [split][E][K][N])
+};
+
+// ------------------------------------------------------------------ tiles
+// Row-tiled modes (NN, NT): wave 0 finds which expert owns this workgroup's
+// row tile.  Tiles are counted per expert as ceil(rows_e / BM); logical tile
+// L = row_tile * ntn + col_tile; workgroup b runs on XCD b % 8 and takes
+// logical tile (b % 8) * ceil(n / 8) + b / 8.
+template <int BM>
+__device__ void find_row_tile(const int32_t* __restrict__ offsets, int E, int ntn, int lane,
+                              int* sh) {
+  int total = 0;
+  for (int c = 0; c < E; c += kWave) {
+    const int e = c + lane;
+    int tiles = 0;
+    if (e < E) tiles = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+    total += wave_sum_int(tiles);
+  }
+  const long long n_act = static_cast<long long>(total) * ntn;
+  const long long per = (n_act + 7) / 8;
+  const long long rank = blockIdx.x >> 3;
+  const long long L = static_cast<long long>(blockIdx.x & 7) * per + rank;
+  int found = 0, e_found = 0, mt_local = 0, nt = 0;
+  if (rank < per && L < n_act) {
+    const int mt = static_cast<int>(L / ntn);
+    nt = static_cast<int>(L - static_cast<long long>(mt) * ntn);
+    int carry = 0;
+    for (int c = 0; c < E; c += kWave) {
+      const int e = c + lane;
+      int tiles = 0;
+      if (e < E) tiles = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+      const int inc = wave_inclusive_scan(tiles, lane);
+      const int excl = carry + inc - tiles;
+      const bool hit = tiles > 0 && mt >= excl && mt < excl + tiles;
+      const uint64_t bal = __ballot(hit);
+      if (bal) {
+        const int srcl = __builtin_ctzll(bal);
+        e_found = __shfl(e, srcl, kWave);
+        mt_local = mt - __shfl(excl, srcl, kWave);
+        found = 1;
+        break;
+      }
+      carry += __shfl(inc, kWave - 1, kWave);
+    }
+  }
+  if (lane == 0) {
+    sh[0] = found;
+    sh[1] = e_found;
+    sh[2] = mt_local;
+    sh[3] = nt;
+  }
+}
+
+struct TileInfo {
+  int e, i0, j0, r_lo, r_hi, g0, g1, slice;
+};
+
+// Returns false if this workgroup has no tile.  Must be called by all threads.
+template <int MODE, int BM>
+__device__ bool resolve_tile(const GemmArgs& p, int* sh, TileInfo& t) {
+  if constexpr (MODE == kTN) {
+    const long long per_e = static_cast<long long>(p.ntm) * p.ntn;
+    const long long n_act = per_e * p.E * p.split;
+    const long long per = (n_act + 7) / 8;
+    const long long rank = blockIdx.x >> 3;
+    const long long L = static_cast<long long>(blockIdx.x & 7) * per + rank;
+    if (rank >= per || L >= n_act) return false;
+    const long long per_slice = per_e * p.E;
+    t.slice = static_cast<int>(L / per_slice);
+    const long long rem0 = L - static_cast<long long>(t.slice) * per_slice;
+    t.e = static_cast<int>(rem0 / per_e);
+    const int rem = static_cast<int>(rem0 - static_cast<long long>(t.e) * per_e);
+    const int mt = rem / p.ntn;
+    const int nt = rem - mt * p.ntn;
+    t.i0 = mt * BM;
+    t.g0 = p.offsets[t.e];
+    t.g1 = p.offsets[t.e + 1];
+    const int len = t.g1 - t.g0;
+    // Slice s reduces rows [g0 + s*chunk, g0 + (s+1)*chunk), chunk a multiple of 64.
+    const int chunk = ((len + p.split - 1) / p.split + 63) / 64 * 64;
+    t.r_lo = min(t.g1, t.g0 + t.slice * chunk);
+    t.r_hi = min(t.g1, t.r_lo + chunk);
+    t.j0 = nt;  // column tile index; scaled by the caller
+    return true;
+  } else {
+    const int lane = threadIdx.x & (kWave - 1);
+    if (threadIdx.x < kWave) find_row_tile<BM>(p.offsets, p.E, p.ntn, lane, sh);
+    __syncthreads();
+    if (!sh[0]) return false;
+    t.e = sh[1];
+    t.g0 = p.offsets[t.e];
+    t.g1 = p.offsets[t.e + 1];
+    t.i0 = t.g0 + sh[2] * BM;
+    t.j0 = sh[3];
+    t.r_lo = 0;
+    t.r_hi = (MODE == kNN) ? p.K : p.N;
+    t.slice = 0;
+    return true;
+  }
+}
+
+// ------------------------------------------------------------------ MFMA path
+constexpr int kBK = 64;        // reduction step per LDS stage
+constexpr int kThreads = 256;  // 4 waves
+
+__device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Operand descriptor: element (o, r) of the tile lives at
+//   direct:     base + o_abs * ld + r_abs    (r contiguous)
+//   transposed: base + r_abs * ld + o_abs    (o contiguous)
+struct Operand {
+  const uint16_t* base;
+  long long ld;
+  int o0;    // absolute o of tile row 0
+  int olim;  // o_abs < olim is valid
+};
+
+// Direct operand: thread handles O/32 chunks of 16 bytes (8 reduction elements).
+template <int O>
+struct DirectLoader {
+  static constexpr int kRegs = O * (kBK / 8) / kThreads;
+  u32x4 v[kRegs];
+
+  __device__ void load(const Operand& op, int r0, int r_hi) {
+#pragma unroll
+    for (int q = 0; q < kRegs; ++q) {
+      const int c = threadIdx.x + q * kThreads;
+      const int o = c >> 3, rc = c & 7;
+      const int oa = op.o0 + o;
+      const int ra = r0 + rc * 8;
+      if (oa < op.olim && ra + 8 <= r_hi)
+        v[q] = ldg16(op.base + static_cast<long long>(oa) * op.ld + ra);
+      else
+        v[q] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ void store(uint16_t* lds) const {
+#pragma unroll
+    for (int q = 0; q < kRegs; ++q) {
+      const int c = threadIdx.x + q * kThreads;
+      const int o = c >> 3, rc = c & 7;
+      *reinterpret_cast<u32x4*>(lds + o * kBK + ((rc ^ (o & 7)) << 3)) = v[q];
+    }
+  }
+};
+
+// Transposed operand: 8x8 blocks (8 reduction rows x 8 contiguous o), one per
+// participating thread; lanes 8i..8i+7 share o-block and take the 8
+// reduction blocks, so each global load instruction reads 8 rows x 128 B and
+// each LDS write hits 8 distinct 16-byte chunks of one row.
+template <int O>
+struct TransLoader {
+  static constexpr int kBlocks = O * kBK / 64;  // 8x8 blocks per tile
+  static_assert(kBlocks <= kThreads, "one block per thread at most");
+  u32x4 v[8];
+
+  __device__ void load(const Operand& op, int r0, int r_hi) {
+    const int b = threadIdx.x;
+    if (b >= kBlocks) return;
+    const int ob = b >> 3, rb = b & 7;
+    const int oa = op.o0 + ob * 8;
+    const bool ovalid = oa + 8 <= op.olim;
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) {
+      const int ra = r0 + rb * 8 + ii;
+      if (ovalid && ra < r_hi)
+        v[ii] = ldg16(op.base + static_cast<long long>(ra) * op.ld + oa);
+      else
+        v[ii] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ void store(uint16_t* lds) const {
+    const int b = threadIdx.x;
+    if (b >= kBlocks) return;
+    const int ob = b >> 3, rb = b & 7;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int q = jj >> 1;
+      u32x4 w;
+#pragma unroll
+      for (int p2 = 0; p2 < 4; ++p2) {
+        const uint32_t a0 = v[2 * p2][q], a1 = v[2 * p2 + 1][q];
+        w[p2] = (jj & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
+      }
+      const int o = ob * 8 + jj;
+      *reinterpret_cast<u32x4*>(lds + o * kBK + ((rb ^ jj) << 3)) = w;
+    }
+  }
+};
+
+template <bool TRANS, int O>
+struct LoaderSel {
+  using type = DirectLoader<O>;
+};
+template <int O>
+struct LoaderSel<true, O> {
+  using type = TransLoader<O>;
+};
+
+__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* lds, int row, int chunk) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * kBK + ((chunk ^ (row & 7)) << 3));
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int MODE, int BM, int BN, typename OutT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p) {
+  constexpr bool XT = (MODE == kTN);
+  constexpr bool YT = (MODE != kNT);
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int MI = WM / 32, NI = WN / 32;
+  constexpr int STAGE = (BM + BN) * kBK;  // bf16 elements per stage
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+  __shared__ int sh[4];
+
+  TileInfo t;
+  if (!resolve_tile<MODE, BM>(p, sh, t)) return;
+  const int j0 = t.j0 * BN;
+  const long long KN = static_cast<long long>(p.K) * p.N;
+
+  Operand xo, yo;
+  if constexpr (MODE == kNN) {
+    xo = {static_cast<const uint16_t*>(p.x), p.K, t.i0, t.g1};
+    yo = {static_cast<const uint16_t*>(p.y) + t.e * KN, p.N, j0, p.N};
+  } else if constexpr (MODE == kNT) {
+    xo = {static_cast<const uint16_t*>(p.x), p.N, t.i0, t.g1};
+    yo = {static_cast<const uint16_t*>(p.y) + t.e * KN, p.N, j0, p.K};
+  } else {
+    xo = {static_cast<const uint16_t*>(p.x), p.K, t.i0, p.K};
+    yo = {static_cast<const uint16_t*>(p.y), p.N, j0, p.N};
+  }
+
+  typename LoaderSel<XT, BM>::type xl;
+  typename LoaderSel<YT, BN>::type yl;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const int wm = wid >> 1, wn = wid & 1;
+
+  f32x16 acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = (t.r_hi - t.r_lo + kBK - 1) / kBK;
+  if (nk > 0) {
+    xl.load(xo, t.r_lo, t.r_hi);
+    yl.load(yo, t.r_lo, t.r_hi);
+    xl.store(lds);
+    yl.store(lds + BM * kBK);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const uint16_t* cur = lds + (kt & 1) * STAGE;
+      const bool more = kt + 1 < nk;
+      if (more) {
+        const int r0 = t.r_lo + (kt + 1) * kBK;
+        xl.load(xo, r0, t.r_hi);
+        yl.load(yo, r0, t.r_hi);
+      }
+#pragma unroll
+      for (int kk = 0; kk < kBK / 16; ++kk) {
+        const int chunk = kk * 2 + (lane >> 5);
+        bf16x8 af[MI], bfr[NI];
+#pragma unroll
+        for (int i = 0; i < MI; ++i) af[i] = lds_frag(cur, wm * WM + i * 32 + (lane & 31), chunk);
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+          bfr[j] = lds_frag(cur + BM * kBK, wn * WN + j * 32 + (lane & 31), chunk);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NI; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+      if (more) {
+        uint16_t* nxt = lds + ((kt + 1) & 1) * STAGE;
+        xl.store(nxt);
+        yl.store(nxt + BM * kBK);
+      }
+      __syncthreads();
+    }
+  }
+
+  // Epilogue.  32x32 accumulator layout: lane l, register r holds
+  // row (r/4)*8 + (l/32)*4 + r%4, column l%32.
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int col = wn * WN + j * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        float v = acc[i][j][r];
+        if constexpr (MODE == kNN) {
+          const int ra = t.i0 + row, ca = j0 + col;
+          if (ra < t.g1 && ca < p.N) {
+            const long long o = static_cast<long long>(ra) * p.N + ca;
+            if constexpr (sizeof(OutT) == 2)
+              static_cast<uint16_t*>(p.out)[o] = f32_to_bf16(v);
+            else
+              static_cast<float*>(p.out)[o] = v;
+          }
+        } else if constexpr (MODE == kNT) {
+          const int ra = t.i0 + row, ca = j0 + col;
+          if (ra < t.g1 && ca < p.K) {
+            const long long o = static_cast<long long>(ra) * p.K + ca;
+            if (p.add) v += bf16_to_f32(static_cast<const uint16_t*>(p.add)[o]);
+            static_cast<uint16_t*>(p.out)[o] = f32_to_bf16(v);
+          }
+        } else {
+          const int ra = t.i0 + row, ca = j0 + col;
+          if (ra < p.K && ca < p.N) {
+            const long long o = (static_cast<long long>(t.slice) * p.E + t.e) * KN +
+                                static_cast<long long>(ra) * p.N + ca;
+            static_cast<float*>(p.out)[o] = v;
+          }
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ FMA path
+template <typename T>
+__device__ __forceinline__ float to_f32(T v);
+template <>
+__device__ __forceinline__ float to_f32<float>(float v) {
+  return v;
+}
+template <>
+__device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) {
+  return bf16_to_f32(v);
+}
+
+constexpr int kSimtTile = 64;
+constexpr int kSimtBK = 16;
+
+template <int MODE, typename InT, typename OutT>
+__global__ __launch_bounds__(kThreads) void gemm_simt_kernel(GemmArgs p) {
+  __shared__ float xs[kSimtBK][kSimtTile + 4];
+  __shared__ float ys[kSimtBK][kSimtTile + 4];
+  __shared__ int sh[4];
+  TileInfo t;
+  if (!resolve_tile<MODE, kSimtTile>(p, sh, t)) return;
+  const int j0 = t.j0 * kSimtTile;
+  const long long KN = static_cast<long long>(p.K) * p.N;
+  const InT* X = static_cast<const InT*>(p.x);
+  const InT* Y = static_cast<const InT*>(p.y);
+  // (o, r) addressing as in the MFMA path.
+  long long xld, yld;
+  int xolim, yolim;
+  bool xt, yt;
+  if (MODE == kNN) {
+    xld = p.K; xolim = t.g1; xt = false;
+    Y += t.e * KN; yld = p.N; yolim = p.N; yt = true;
+  } else if (MODE == kNT) {
+    xld = p.N; xolim = t.g1; xt = false;
+    Y += t.e * KN; yld = p.N; yolim = p.K; yt = false;
+  } else {
+    xld = p.K; xolim = p.K; xt = true;
+    yld = p.N; yolim = p.N; yt = true;
+  }
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+
+  for (int r0 = t.r_lo; r0 < t.r_hi; r0 += kSimtBK) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = threadIdx.x + q * kThreads;
+      // direct: r fastest (contiguous); transposed: o fastest.
+      int o, r;
+      if (!xt) { o = idx / kSimtBK; r = idx % kSimtBK; } else { o = idx % kSimtTile; r = idx / kSimtTile; }
+      int oa = t.i0 + o, ra = r0 + r;
+      float v = 0.f;
+      if (oa < xolim && ra < t.r_hi)
+        v = to_f32(xt ? X[static_cast<long long>(ra) * xld + oa] : X[static_cast<long long>(oa) * xld + ra]);
+      xs[r][o] = v;
+      if (!yt) { o = idx / kSimtBK; r = idx % kSimtBK; } else { o = idx % kSimtTile; r = idx / kSimtTile; }
+      oa = j0 + o;
+      ra = r0 + r;
+      v = 0.f;
+      if (oa < yolim && ra < t.r_hi)
+        v = to_f32(yt ? Y[static_cast<long long>(ra) * yld + oa] : Y[static_cast<long long>(oa) * yld + ra]);
+      ys[r][o] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kSimtBK; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = xs[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = ys[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = ty * 4 + i, col = tx * 4 + j;
+      const int ra = t.i0 + row, ca = j0 + col;
+      float v = acc[i][j];
+      if (MODE == kNN) {
+        if (ra < t.g1 && ca < p.N) {
+          const long long o = static_cast<long long>(ra) * p.N + ca;
+          if constexpr (sizeof(OutT) == 2) static_cast<uint16_t*>(p.out)[o] = f32_to_bf16(v);
+          else static_cast<float*>(p.out)[o] = v;
+        }
+      } else if (MODE == kNT) {
+        if (ra < t.g1 && ca < p.K) {
+          const long long o = static_cast<long long>(ra) * p.K + ca;
+          if (p.add) v += to_f32(static_cast<const InT*>(p.add)[o]);
+          if constexpr (sizeof(OutT) == 2) static_cast<uint16_t*>(p.out)[o] = f32_to_bf16(v);
+          else static_cast<float*>(p.out)[o] = v;
+        }
+      } else {
+        if (ra < p.K && ca < p.N)
+          static_cast<float*>(p.out)[t.e * KN + static_cast<long long>(ra) * p.N + ca] = v;
+      }
+    }
+  }
+}
+
+// Sum of split-K partials: db[i] = sum_s part[s][i], in increasing s.
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part,
+                                                           long long n, int split,
+                                                           float* __restrict__ db) {
+  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += gridDim.x * 256LL) {
+    float s = 0.f;
+    for (int q = 0; q < split; ++q) s += part[q * n + i];
+    db[i] = s;
+  }
+}
+
+// ------------------------------------------------------------------ host side
+struct Cfg {
+  int bm, bn;
+};
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+// Tile shape for the row-tiled modes from the mean rows per expert and the
+// number of output columns.
+Cfg pick_row_cfg(int M, int E, int ncols) {
+  const double mean = static_cast<double>(M) / E;
+  if (ncols <= 64) return {64, 64};
+  if (mean < 96.0) return ncols >= 256 ? Cfg{64, 256} : Cfg{64, 64};
+  const long long tiles256 = (ceil_div(M, 256) + E) * ceil_div(ncols, 256);
+  if (tiles256 >= 512) return {256, 256};
+  return {128, 128};
+}
+
+Cfg pick_tn_cfg(int K, int N, int E) {
+  if (N <= 64 || K <= 64) return {64, 64};
+  const long long tiles256 = ceil_div(K, 256) * ceil_div(N, 256) * E;
+  if (tiles256 >= 512) return {256, 256};
+  return {128, 128};
+}
+
+int pick_split(int M, int K, int N, int E) {
+  const Cfg c = pick_tn_cfg(K, N, E);
+  const long long tiles = ceil_div(K, c.bm) * ceil_div(N, c.bn) * E;
+  if (tiles >= 512) return 1;
+  const long long mean_rows = M / E;
+  long long s = ceil_div(512, tiles);
+  const long long by_rows = mean_rows / 256;  // at least 4 stages of 64 rows per slice
+  if (s > by_rows) s = by_rows;
+  if (s > 64) s = 64;
+  return static_cast<int>(s < 1 ? 1 : s);
+}
+
+bool mfma_ok(moe_dtype dt, int K, int N) { return dt == MOE_BF16 && K % 8 == 0 && N % 8 == 0; }
+
+template <int MODE, int BM, int BN, typename OutT>
+void launch_mfma(GemmArgs p, long long tiles_upper, hipStream_t st) {
+  const long long grid = ceil_div(tiles_upper, 8) * 8;
+  hipLaunchKernelGGL((gemm_mfma_kernel<MODE, BM, BN, OutT>), dim3(static_cast<unsigned>(grid)),
+                     dim3(kThreads), 0, st, p);
+}
+
+template <int MODE, typename OutT>
+void dispatch_mfma(Cfg c, GemmArgs p, long long rows_tiles_upper_fn_M, hipStream_t st) {
+  (void)rows_tiles_upper_fn_M;
+  const int ncols = (MODE == kNN) ? p.N : (MODE == kNT ? p.K : p.N);
+  p.ntn = static_cast<int>(ceil_div(ncols, c.bn));
+  long long upper;
+  if (MODE == kTN) {
+    p.ntm = static_cast<int>(ceil_div(p.K, c.bm));
+    upper = static_cast<long long>(p.ntm) * p.ntn * p.E * p.split;
+  } else {
+    upper = (ceil_div(p.M, c.bm) + p.E) * p.ntn;
+  }
+  if (c.bm == 256 && c.bn == 256) launch_mfma<MODE, 256, 256, OutT>(p, upper, st);
+  else if (c.bm == 128 && c.bn == 128) launch_mfma<MODE, 128, 128, OutT>(p, upper, st);
+  else if (c.bm == 64 && c.bn == 256) launch_mfma<MODE, 64, 256, OutT>(p, upper, st);
+  else launch_mfma<MODE, 64, 64, OutT>(p, upper, st);
+}
+
+template <int MODE, typename InT, typename OutT>
+void launch_simt(GemmArgs p, hipStream_t st) {
+  const int ncols = (MODE == kNN) ? p.N : (MODE == kNT ? p.K : p.N);
+  p.ntn = static_cast<int>(ceil_div(ncols, kSimtTile));
+  p.split = 1;
+  long long upper;
+  if (MODE == kTN) {
+    p.ntm = static_cast<int>(ceil_div(p.K, kSimtTile));
+    upper = static_cast<long long>(p.ntm) * p.ntn * p.E;
+  } else {
+    upper = (ceil_div(p.M, kSimtTile) + p.E) * p.ntn;
+  }
+  const long long grid = ceil_div(upper, 8) * 8;
+  hipLaunchKernelGGL((gemm_simt_kernel<MODE, InT, OutT>), dim3(static_cast<unsigned>(grid)),
+                     dim3(kThreads), 0, st, p);
+}
+
+moe_status check_gemm(const void* offsets, int M, int K, int N, int E, moe_dtype dt) {
+  MOE_REQUIRE(offsets != nullptr, MOE_ERR_INVALID_ARG, "grouped gemm: null offsets");
+  MOE_REQUIRE(M >= 1 && K >= 1 && N >= 1 && E >= 1, MOE_ERR_INVALID_ARG,
+              "grouped gemm: M, K, N, E must be >= 1");
+  MOE_REQUIRE(dtype_ok(dt), MOE_ERR_UNSUPPORTED, "grouped gemm: unknown dtype");
+  MOE_REQUIRE(static_cast<long long>(M) * (K > N ? K : N) < (1ll << 40), MOE_ERR_UNSUPPORTED,
+              "grouped gemm: operand too large");
+  MOE_REQUIRE(static_cast<long long>(E) * K * N < (1ll << 40), MOE_ERR_UNSUPPORTED,
+              "grouped gemm: weight tensor too large");
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_grouped_gemm_workspace_size(int M, int K, int N, int E, moe_dtype dtype) {
+  if (M < 1 || K < 1 || N < 1 || E < 1 || !mfma_ok(dtype, K, N)) return 0;
+  const int s = pick_split(M, K, N, E);
+  if (s <= 1) return 0;
+  return static_cast<size_t>(s) * E * K * N * sizeof(float);
+}
+
+extern "C" moe_status moe_grouped_gemm_fwd(const void* a, const void* b, const int32_t* offsets,
+                                           int M, int K, int N, int E, moe_dtype ab_dtype,
+                                           void* c, moe_dtype c_dtype, void* ws, size_t ws_bytes,
+                                           moe_stream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  clear_error();
+  if (moe_status s = check_gemm(offsets, M, K, N, E, ab_dtype)) return s;
+  MOE_REQUIRE(a && b && c, MOE_ERR_INVALID_ARG, "moe_grouped_gemm_fwd: null pointer");
+  MOE_REQUIRE(dtype_ok(c_dtype), MOE_ERR_UNSUPPORTED, "moe_grouped_gemm_fwd: bad c_dtype");
+  MOE_REQUIRE(!(ab_dtype == MOE_F32 && c_dtype == MOE_BF16), MOE_ERR_UNSUPPORTED,
+              "moe_grouped_gemm_fwd: float32 inputs need a float32 output");
+  GemmArgs p{a, b, nullptr, c, offsets, M, K, N, E, 0, 0, 1};
+  hipStream_t st = as_stream(stream);
+  if (mfma_ok(ab_dtype, K, N)) {
+    const Cfg cfg = pick_row_cfg(M, E, N);
+    if (c_dtype == MOE_BF16) dispatch_mfma<kNN, uint16_t>(cfg, p, 0, st);
+    else dispatch_mfma<kNN, float>(cfg, p, 0, st);
+  } else if (ab_dtype == MOE_BF16) {
+    if (c_dtype == MOE_BF16) launch_simt<kNN, uint16_t, uint16_t>(p, st);
+    else launch_simt<kNN, uint16_t, float>(p, st);
+  } else {
+    launch_simt<kNN, float, float>(p, st);
+  }
+  return check_launch("moe_grouped_gemm_fwd");
+}
+
+extern "C" moe_status moe_grouped_gemm_bwd(const void* a, const void* b, const void* dc,
+                                           const int32_t* offsets, int M, int K, int N, int E,
+                                           moe_dtype dtype, void* da, const void* da_add,
+                                           float* db, void* ws, size_t ws_bytes,
+                                           moe_stream_t stream) {
+  clear_error();
+  if (moe_status s = check_gemm(offsets, M, K, N, E, dtype)) return s;
+  MOE_REQUIRE(dc != nullptr, MOE_ERR_INVALID_ARG, "moe_grouped_gemm_bwd: null dc");
+  MOE_REQUIRE(da == nullptr || b != nullptr, MOE_ERR_INVALID_ARG,
+              "moe_grouped_gemm_bwd: da needs b");
+  MOE_REQUIRE(db == nullptr || a != nullptr, MOE_ERR_INVALID_ARG,
+              "moe_grouped_gemm_bwd: db needs a");
+  const bool use_mfma = mfma_ok(dtype, K, N);
+  int split = 1;
+  if (db && use_mfma) {
+    split = pick_split(M, K, N, E);
+    if (split > 1) {
+      const size_t need = moe_grouped_gemm_workspace_size(M, K, N, E, dtype);
+      MOE_REQUIRE(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE,
+                  "moe_grouped_gemm_bwd: workspace too small");
+      MOE_REQUIRE((reinterpret_cast<uintptr_t>(ws) & 15) == 0, MOE_ERR_WORKSPACE,
+                  "moe_grouped_gemm_bwd: workspace must be 16-byte aligned");
+    }
+  }
+  hipStream_t st = as_stream(stream);
+  if (da) {
+    GemmArgs p{dc, b, da_add, da, offsets, M, K, N, E, 0, 0, 1};
+    if (use_mfma) {
+      dispatch_mfma<kNT, uint16_t>(pick_row_cfg(M, E, K), p, 0, st);
+    } else if (dtype == MOE_BF16) {
+      launch_simt<kNT, uint16_t, uint16_t>(p, st);
+    } else {
+      launch_simt<kNT, float, float>(p, st);
+    }
+    if (moe_status s = check_launch("moe_grouped_gemm_bwd/da")) return s;
+  }
+  if (db) {
+    if (use_mfma) {
+      GemmArgs p{a, dc, nullptr, split > 1 ? ws : static_cast<void*>(db), offsets, M, K, N, E,
+                 0, 0, split};
+      dispatch_mfma<kTN, float>(pick_tn_cfg(K, N, E), p, 0, st);
+      if (moe_status s = check_launch("moe_grouped_gemm_bwd/db")) return s;
+      if (split > 1) {
+        const long long n = static_cast<long long>(E) * K * N;
+        long long g = ceil_div(n, 256);
+        if (g > 8192) g = 8192;
+        hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<unsigned>(g)), dim3(256), 0, st,
+                           static_cast<const float*>(ws), n, split, db);
+      }
+    } else {
+      GemmArgs p{a, dc, nullptr, db, offsets, M, K, N, E, 0, 0, 1};
+      if (dtype == MOE_BF16) launch_simt<kTN, uint16_t, float>(p, st);
+      else launch_simt<kTN, float, float>(p, st);
+    }
+    if (moe_status s = check_launch("moe_grouped_gemm_bwd/db")) return s;
+  }
+  return MOE_OK;
+}

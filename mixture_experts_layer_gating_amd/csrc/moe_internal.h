@@ -1,0 +1,97 @@
+// Internal helpers shared by the library's translation units: error state,
+// argument checks, bf16 conversion and wave-level primitives for gfx950
+// (64-lane wavefronts).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- errors
+void set_error(const std::string& msg);
+void clear_error();
+
+inline moe_status fail(moe_status st, const std::string& msg) {
+  set_error(msg);
+  return st;
+}
+
+// Checks the launch that was just enqueued.
+moe_status check_launch(const char* what);
+
+#define MOE_REQUIRE(cond, status, msg)             \
+  do {                                             \
+    if (!(cond)) return ::moe::fail((status), (msg)); \
+  } while (0)
+
+inline hipStream_t as_stream(moe_stream_t s) {
+  return reinterpret_cast<hipStream_t>(s);
+}
+
+inline size_t dtype_size(moe_dtype t) { return t == MOE_BF16 ? 2 : 4; }
+inline bool dtype_ok(moe_dtype t) { return t == MOE_F32 || t == MOE_BF16; }
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16
+// bf16 values are carried as raw 16-bit patterns.
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// Round to nearest, ties to even; NaN stays NaN (quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Two floats -> two packed bf16 in one dword (lo = a, hi = b).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) |
+         (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ---------------------------------------------------------------- wave ops
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Inclusive prefix sum across the 64 lanes.
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int n = __shfl_up(v, o, kWave);
+    if (lane >= o) v += n;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) {
+  return (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+}
+
+}  // namespace moe

@@ -1,0 +1,219 @@
+// Token permutation into expert-contiguous order, the weighted combine back
+// to token order, and the combine's backward pass.
+//
+// The grouped GEMM consumes the tokens of each expert as one contiguous block
+// of rows [Brief, Core method]; these kernels move rows between token order
+// and that expert-sorted order.  They are HBM-bound: every thread moves
+// 16-byte chunks, consecutive threads take consecutive chunks of a row, so
+// each row is read and written as whole cache lines.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kMoveBlock = 256;
+
+struct alignas(16) Vec16 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ Vec16 ld16(const void* p) {
+  return *reinterpret_cast<const Vec16*>(p);
+}
+__device__ __forceinline__ void st16(void* p, const Vec16& v) {
+  *reinterpret_cast<Vec16*>(p) = v;
+}
+
+// Elements per 16-byte chunk: 8 bf16 or 4 fp32.
+template <typename T>
+struct Chunk;
+template <>
+struct Chunk<uint16_t> {
+  static constexpr int N = 8;
+  __device__ static void unpack(const Vec16& v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = lo_bf16(v.w[i]);
+      f[2 * i + 1] = hi_bf16(v.w[i]);
+    }
+  }
+  __device__ static Vec16 pack(const float* f) {
+    Vec16 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v.w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+    return v;
+  }
+};
+template <>
+struct Chunk<float> {
+  static constexpr int N = 4;
+  __device__ static void unpack(const Vec16& v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v.w[i]);
+  }
+  __device__ static Vec16 pack(const float* f) {
+    Vec16 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v.w[i] = __float_as_uint(f[i]);
+    return v;
+  }
+};
+
+// xp[p, :] = x[src[p] / k, :]; grid-stride over (row, chunk) pairs.
+__global__ __launch_bounds__(kMoveBlock) void permute_kernel(const char* __restrict__ x,
+                                                             const int32_t* __restrict__ src,
+                                                             long long rows, int k,
+                                                             int chunks_per_row,
+                                                             char* __restrict__ xp) {
+  const long long total = rows * chunks_per_row;
+  const size_t row_bytes = static_cast<size_t>(chunks_per_row) * 16;
+  for (long long i = blockIdx.x * static_cast<long long>(kMoveBlock) + threadIdx.x; i < total;
+       i += static_cast<long long>(gridDim.x) * kMoveBlock) {
+    const long long p = i / chunks_per_row;
+    const int c = static_cast<int>(i - p * chunks_per_row);
+    const int t = src[p] / k;
+    st16(xp + p * row_bytes + c * 16, ld16(x + static_cast<size_t>(t) * row_bytes + c * 16));
+  }
+}
+
+// y[t, :] = sum_j w[t, j] * yp[dest[t*k + j], :]  (w == nullptr -> weight 1)
+// with fp32 accumulation in increasing j.
+template <typename T>
+__global__ __launch_bounds__(kMoveBlock) void unpermute_kernel(const char* __restrict__ yp,
+                                                               const int32_t* __restrict__ dest,
+                                                               const float* __restrict__ w,
+                                                               int Tn, int k, int chunks_per_row,
+                                                               char* __restrict__ y) {
+  constexpr int N = Chunk<T>::N;
+  const long long total = static_cast<long long>(Tn) * chunks_per_row;
+  const size_t row_bytes = static_cast<size_t>(chunks_per_row) * 16;
+  for (long long i = blockIdx.x * static_cast<long long>(kMoveBlock) + threadIdx.x; i < total;
+       i += static_cast<long long>(gridDim.x) * kMoveBlock) {
+    const int t = static_cast<int>(i / chunks_per_row);
+    const int c = static_cast<int>(i - static_cast<long long>(t) * chunks_per_row);
+    float acc[N];
+#pragma unroll
+    for (int q = 0; q < N; ++q) acc[q] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const size_t s = static_cast<size_t>(t) * k + j;
+      const int r = dest[s];
+      const float wt = w ? w[s] : 1.f;
+      float v[N];
+      Chunk<T>::unpack(ld16(yp + static_cast<size_t>(r) * row_bytes + c * 16), v);
+#pragma unroll
+      for (int q = 0; q < N; ++q) acc[q] = fmaf(wt, v[q], acc[q]);
+    }
+    st16(y + static_cast<size_t>(t) * row_bytes + c * 16, Chunk<T>::pack(acc));
+  }
+}
+
+// One block per token: dyp rows of its k slots and the k dot products dw.
+template <typename T>
+__global__ __launch_bounds__(kMoveBlock) void unpermute_bwd_kernel(
+    const char* __restrict__ dy, const char* __restrict__ yp, const int32_t* __restrict__ dest,
+    const float* __restrict__ w, int k, int chunks_per_row, char* __restrict__ dyp,
+    float* __restrict__ dw) {
+  constexpr int N = Chunk<T>::N;
+  __shared__ float part[kMoveBlock / kWave][MOE_MAX_TOPK];
+  const int t = blockIdx.x;
+  const size_t row_bytes = static_cast<size_t>(chunks_per_row) * 16;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const char* dyrow = dy + static_cast<size_t>(t) * row_bytes;
+  for (int j = 0; j < k; ++j) {
+    const size_t s = static_cast<size_t>(t) * k + j;
+    const int r = dest[s];
+    const float wt = w[s];
+    float dot = 0.f;
+    for (int c = threadIdx.x; c < chunks_per_row; c += kMoveBlock) {
+      float g[N], v[N], o[N];
+      Chunk<T>::unpack(ld16(dyrow + c * 16), g);
+      Chunk<T>::unpack(ld16(yp + static_cast<size_t>(r) * row_bytes + c * 16), v);
+#pragma unroll
+      for (int q = 0; q < N; ++q) {
+        dot = fmaf(g[q], v[q], dot);
+        o[q] = wt * g[q];
+      }
+      st16(dyp + static_cast<size_t>(r) * row_bytes + c * 16, Chunk<T>::pack(o));
+    }
+    dot = wave_sum(dot);
+    if (lane == 0) part[wid][j] = dot;
+  }
+  __syncthreads();
+  if (threadIdx.x < k) {
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < kMoveBlock / kWave; ++q) s += part[q][threadIdx.x];
+    dw[static_cast<size_t>(t) * k + threadIdx.x] = s;
+  }
+}
+
+int move_grid(long long work_items) {
+  // Enough blocks to cover the work, capped at 32 per compute unit (256 CUs).
+  long long b = (work_items + kMoveBlock - 1) / kMoveBlock;
+  if (b > 256LL * 32) b = 256LL * 32;
+  return static_cast<int>(b < 1 ? 1 : b);
+}
+
+moe_status check_move(int T, int k, int d, moe_dtype dt) {
+  MOE_REQUIRE(T >= 1 && k >= 1 && d >= 1, MOE_ERR_INVALID_ARG, "T, k, d must be >= 1");
+  MOE_REQUIRE(k <= MOE_MAX_TOPK, MOE_ERR_UNSUPPORTED, "k exceeds 32");
+  MOE_REQUIRE(dtype_ok(dt), MOE_ERR_UNSUPPORTED, "unknown dtype");
+  MOE_REQUIRE(d % 8 == 0, MOE_ERR_UNSUPPORTED, "d must be a multiple of 8");
+  MOE_REQUIRE(static_cast<long long>(T) * k < (1ll << 31), MOE_ERR_UNSUPPORTED,
+              "T*k must be < 2^31");
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" moe_status moe_permute(const void* x, const int32_t* src, int T, int k, int d,
+                                  moe_dtype dtype, void* xp, moe_stream_t stream) {
+  clear_error();
+  if (moe_status s = check_move(T, k, d, dtype)) return s;
+  MOE_REQUIRE(x && src && xp, MOE_ERR_INVALID_ARG, "moe_permute: null pointer");
+  const int cpr = static_cast<int>(d * dtype_size(dtype) / 16);
+  const long long rows = static_cast<long long>(T) * k;
+  hipLaunchKernelGGL(permute_kernel, dim3(move_grid(rows * cpr)), dim3(kMoveBlock), 0,
+                     as_stream(stream), static_cast<const char*>(x), src, rows, k, cpr,
+                     static_cast<char*>(xp));
+  return check_launch("moe_permute");
+}
+
+extern "C" moe_status moe_unpermute(const void* yp, const int32_t* dest, const float* w, int T,
+                                    int k, int d, moe_dtype dtype, void* y, moe_stream_t stream) {
+  clear_error();
+  if (moe_status s = check_move(T, k, d, dtype)) return s;
+  MOE_REQUIRE(yp && dest && y, MOE_ERR_INVALID_ARG, "moe_unpermute: null pointer");
+  const int cpr = static_cast<int>(d * dtype_size(dtype) / 16);
+  const dim3 grid(move_grid(static_cast<long long>(T) * cpr));
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(unpermute_kernel<uint16_t>, grid, dim3(kMoveBlock), 0, as_stream(stream),
+                       static_cast<const char*>(yp), dest, w, T, k, cpr, static_cast<char*>(y));
+  else
+    hipLaunchKernelGGL(unpermute_kernel<float>, grid, dim3(kMoveBlock), 0, as_stream(stream),
+                       static_cast<const char*>(yp), dest, w, T, k, cpr, static_cast<char*>(y));
+  return check_launch("moe_unpermute");
+}
+
+extern "C" moe_status moe_unpermute_bwd(const void* dy, const void* yp, const int32_t* dest,
+                                        const float* w, int T, int k, int d, moe_dtype dtype,
+                                        void* dyp, float* dw, moe_stream_t stream) {
+  clear_error();
+  if (moe_status s = check_move(T, k, d, dtype)) return s;
+  MOE_REQUIRE(dy && yp && dest && w && dyp && dw, MOE_ERR_INVALID_ARG,
+              "moe_unpermute_bwd: null pointer");
+  const int cpr = static_cast<int>(d * dtype_size(dtype) / 16);
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(unpermute_bwd_kernel<uint16_t>, dim3(T), dim3(kMoveBlock), 0,
+                       as_stream(stream), static_cast<const char*>(dy),
+                       static_cast<const char*>(yp), dest, w, k, cpr, static_cast<char*>(dyp), dw);
+  else
+    hipLaunchKernelGGL(unpermute_bwd_kernel<float>, dim3(T), dim3(kMoveBlock), 0,
+                       as_stream(stream), static_cast<const char*>(dy),
+                       static_cast<const char*>(yp), dest, w, k, cpr, static_cast<char*>(dyp), dw);
+  return check_launch("moe_unpermute_bwd");
+}

@@ -1,0 +1,145 @@
+"""Forward and backward pass of one MoE layer, composed from the C-ABI calls.
+
+Every arithmetic step runs in the HIP library; this module only owns the
+device buffers (allocated once through torch) and sequences the calls on one
+stream.  No host synchronisation happens inside a pass: the per-expert
+offsets produced by counting stay on the device and are read there by the
+grouped GEMMs.
+
+Forward (expert selection, then expert computation [Summary, Method details /
+technical framework]; counting, indexing and the grouped GEMM [Brief, Core
+method]):
+
+    logits = x @ wr                    moe_grouped_gemm_fwd (one group, fp32 out)
+    idx, w, p = top-k softmax          moe_route_topk
+    counts, offsets, dest, src         moe_count_index
+    xp = x[src // k]                   moe_permute
+    h  = xp @ W1[e]                    moe_grouped_gemm_fwd
+    a  = silu(h_gate) * h_up           moe_act_fwd
+    yp = a @ W2[e]                     moe_grouped_gemm_fwd
+    y  = sum_j w * yp[dest]            moe_unpermute
+
+Backward of <y, dy> (the forward-plus-backward unit of [Brief, Key results]):
+
+    dyp, dw   moe_unpermute_bwd           da, dW2   moe_grouped_gemm_bwd
+    dh        moe_act_bwd                 dxp, dW1  moe_grouped_gemm_bwd
+    dx_e      moe_unpermute (w = NULL)    dlogits   moe_route_topk_bwd
+    dx = dx_e + dlogits @ wr^T, dwr = x^T @ dlogits   moe_grouped_gemm_bwd
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import torch
+
+from . import _lib as L
+
+
+@dataclasses.dataclass
+class Grads:
+    dx: torch.Tensor
+    dwr: torch.Tensor
+    dw1: torch.Tensor
+    dw2: torch.Tensor
+
+
+class MoELayer:
+    """Buffers and call sequence for a fixed shape (T, d, E, k, F, dtype).
+
+    ``dtype`` is ``torch.bfloat16`` (fp32 accumulation inside the kernels) or
+    ``torch.float32``.  Inputs are passed to :meth:`forward`; the returned
+    tensors are views of buffers owned by the layer and are overwritten by the
+    next call.
+    """
+
+    def __init__(self, T, d, E, k, F, dtype=torch.bfloat16, device="cuda", renorm=False):
+        if not (1 <= k <= E):
+            raise ValueError("need 1 <= k <= E")
+        self.T, self.d, self.E, self.k, self.F = T, d, E, k, F
+        self.dtype = dtype
+        self.code = L.dtype_code(dtype)
+        self.renorm = bool(renorm)
+        self.device = torch.device(device)
+        Tk = T * k
+        self.Tk = Tk
+        dev = self.device
+        f32, i32 = torch.float32, torch.int32
+        # routing
+        self.logits = torch.empty(T, E, dtype=f32, device=dev)
+        self.idx = torch.empty(T, k, dtype=i32, device=dev)
+        self.w = torch.empty(T, k, dtype=f32, device=dev)
+        self.probs = torch.empty(T, E, dtype=f32, device=dev)
+        self.counts = torch.empty(E, dtype=i32, device=dev)
+        self.offsets = torch.empty(E + 1, dtype=i32, device=dev)
+        self.dest = torch.empty(Tk, dtype=i32, device=dev)
+        self.src = torch.empty(Tk, dtype=i32, device=dev)
+        self.router_offsets = torch.tensor([0, T], dtype=i32, device=dev)
+        ci_ws = L.moe_count_index_workspace_size(T, k, E)
+        self.ci_ws = torch.empty(max(ci_ws, 16), dtype=torch.uint8, device=dev)
+        # expert activations (expert-sorted rows)
+        self.xp = torch.empty(Tk, d, dtype=dtype, device=dev)
+        self.h = torch.empty(Tk, 2 * F, dtype=dtype, device=dev)
+        self.a = torch.empty(Tk, F, dtype=dtype, device=dev)
+        self.yp = torch.empty(Tk, d, dtype=dtype, device=dev)
+        self.y = torch.empty(T, d, dtype=dtype, device=dev)
+        # backward
+        self.dyp = torch.empty(Tk, d, dtype=dtype, device=dev)
+        self.dw = torch.empty(T, k, dtype=f32, device=dev)
+        self.da = torch.empty(Tk, F, dtype=dtype, device=dev)
+        self.dh = torch.empty(Tk, 2 * F, dtype=dtype, device=dev)
+        self.dxp = torch.empty(Tk, d, dtype=dtype, device=dev)
+        self.dx_e = torch.empty(T, d, dtype=dtype, device=dev)
+        self.dx = torch.empty(T, d, dtype=dtype, device=dev)
+        self.dlogits = torch.empty(T, E, dtype=dtype, device=dev)
+        self.dwr = torch.empty(d, E, dtype=f32, device=dev)
+        self.dw1 = torch.empty(E, d, 2 * F, dtype=f32, device=dev)
+        self.dw2 = torch.empty(E, F, d, dtype=f32, device=dev)
+        # grouped-GEMM workspaces (split reduction partials of the weight grads)
+        c = self.code
+        sizes = [L.moe_grouped_gemm_workspace_size(T, d, E, 1, c),
+                 L.moe_grouped_gemm_workspace_size(Tk, F, d, E, c),
+                 L.moe_grouped_gemm_workspace_size(Tk, d, 2 * F, E, c)]
+        self.gemm_ws_bytes = max(sizes)
+        self.gemm_ws = (torch.empty(self.gemm_ws_bytes, dtype=torch.uint8, device=dev)
+                        if self.gemm_ws_bytes else None)
+        self._inputs = None
+
+    # ------------------------------------------------------------------
+    def forward(self, x, wr, w1, w2, bias=None, forced_idx=None, stream=None):
+        T, d, E, k, F, Tk, c = self.T, self.d, self.E, self.k, self.F, self.Tk, self.code
+        s = stream
+        L.moe_grouped_gemm_fwd(x, wr, self.router_offsets, T, d, E, 1, c, self.logits,
+                               L.MOE_F32, stream=s)
+        L.moe_route_topk(self.logits, bias, T, E, k, self.renorm, forced_idx, self.idx, self.w,
+                         self.probs, stream=s)
+        L.moe_count_index(self.idx, T, k, E, self.counts, self.offsets, self.dest, self.src,
+                          self.ci_ws, self.ci_ws.numel(), stream=s)
+        L.moe_permute(x, self.src, T, k, d, c, self.xp, stream=s)
+        L.moe_grouped_gemm_fwd(self.xp, w1, self.offsets, Tk, d, 2 * F, E, c, self.h, c,
+                               stream=s)
+        L.moe_act_fwd(self.h, Tk, F, c, self.a, stream=s)
+        L.moe_grouped_gemm_fwd(self.a, w2, self.offsets, Tk, F, d, E, c, self.yp, c, stream=s)
+        L.moe_unpermute(self.yp, self.dest, self.w, T, k, d, c, self.y, stream=s)
+        self._inputs = (x, wr, w1, w2)
+        return self.y
+
+    def backward(self, dy, stream=None):
+        if self._inputs is None:
+            raise RuntimeError("backward() before forward()")
+        x, wr, w1, w2 = self._inputs
+        T, d, E, k, F, Tk, c = self.T, self.d, self.E, self.k, self.F, self.Tk, self.code
+        s = stream
+        ws, wsb = self.gemm_ws, self.gemm_ws_bytes
+        L.moe_unpermute_bwd(dy, self.yp, self.dest, self.w, T, k, d, c, self.dyp, self.dw,
+                            stream=s)
+        L.moe_grouped_gemm_bwd(self.a, w2, self.dyp, self.offsets, Tk, F, d, E, c, self.da, None,
+                               self.dw2, ws, wsb, stream=s)
+        L.moe_act_bwd(self.h, self.da, Tk, F, c, self.dh, stream=s)
+        L.moe_grouped_gemm_bwd(self.xp, w1, self.dh, self.offsets, Tk, d, 2 * F, E, c, self.dxp,
+                               None, self.dw1, ws, wsb, stream=s)
+        L.moe_unpermute(self.dxp, self.dest, None, T, k, d, c, self.dx_e, stream=s)
+        L.moe_route_topk_bwd(self.probs, self.idx, self.dw, T, E, k, self.renorm, self.dlogits,
+                             c, stream=s)
+        L.moe_grouped_gemm_bwd(x, wr, self.dlogits, self.router_offsets, T, d, E, 1, c, self.dx,
+                               self.dx_e, self.dwr, ws, wsb, stream=s)
+        return Grads(self.dx, self.dwr, self.dw1, self.dw2)

@@ -1,0 +1,217 @@
+"""GPU parity of the data-movement, activation and grouped-GEMM kernels
+against the CPU oracle on identical (bf16-representable) inputs.
+
+Permutation is a bitwise copy.  Float results: outputs produced by one bf16
+rounding of an fp32 value are held to TOL_ONE_ROUNDING; fp32 outputs to
+1e-5 relative Frobenius."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from moe_inputs import random_topk_ids, round_to_bf16
+from tests._gpu import DEV, TOL_F32, TOL_ONE_ROUNDING, bits, dev, host, rel, say
+
+pytestmark = pytest.mark.gpu
+
+L = None
+
+
+@pytest.fixture(autouse=True)
+def _native_lib():
+    """The HIP library; importing it raises if it is not built (no fallback)."""
+    global L
+    import mixture_experts_layer_gating_amd._lib as lib
+    L = lib
+
+
+DTYPES = {"bf16": torch.bfloat16, "fp32": torch.float32}
+
+
+def _normal(shape, seed, scale=1.0, dtype="bf16"):
+    a = (np.random.default_rng(seed).standard_normal(shape) * scale).astype(np.float32)
+    return round_to_bf16(a) if dtype == "bf16" else a
+
+
+# ------------------------------------------------------------------ permute / combine
+@pytest.mark.parametrize("T,k,E,d", [(1, 1, 1, 8), (37, 2, 5, 24), (1024, 8, 64, 2048),
+                                     (300, 3, 7, 136)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_permute_unpermute(T, k, E, d, dtype):
+    say(f"permute/unpermute T={T} k={k} E={E} d={d} {dtype}")
+    tdt = DTYPES[dtype]
+    code = L.dtype_code(tdt)
+    ids = random_topk_ids(T, k, E, seed=T + d)
+    _, _, dest, src = O.build_index(ids, E)
+    x = _normal((T, d), 1, dtype=dtype)
+    xd = dev(x, tdt)
+    xp = torch.empty(T * k, d, dtype=tdt, device=DEV)
+    L.moe_permute(xd, dev(src), T, k, d, code, xp)
+    torch.cuda.synchronize()
+    want = O.permute(x, src, k).astype(np.float32)
+    if dtype == "bf16":
+        np.testing.assert_array_equal(bits(xp), bits(dev(want, tdt)))
+    else:
+        np.testing.assert_array_equal(host(xp), want)
+    # combine with weights, and with unit weights (the permute's backward)
+    yp = _normal((T * k, d), 2, dtype=dtype)
+    w = np.random.default_rng(3).random((T, k)).astype(np.float32)
+    y = torch.empty(T, d, dtype=tdt, device=DEV)
+    tol = TOL_ONE_ROUNDING if dtype == "bf16" else TOL_F32
+    for wt in (w, None):
+        L.moe_unpermute(dev(yp, tdt), dev(dest), None if wt is None else dev(wt), T, k, d, code, y)
+        torch.cuda.synchronize()
+        ref = O.combine(yp, dest, np.ones((T, k)) if wt is None else wt, k)
+        assert rel(host(y), ref) <= tol
+    # combine backward
+    dy = _normal((T, d), 4, dtype=dtype)
+    dyp = torch.empty(T * k, d, dtype=tdt, device=DEV)
+    dw = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    L.moe_unpermute_bwd(dev(dy, tdt), dev(yp, tdt), dev(dest), dev(w), T, k, d, code, dyp, dw)
+    torch.cuda.synchronize()
+    rdyp, rdw = O.combine_backward(dy, yp, dest, w, k)
+    assert rel(host(dyp), rdyp) <= tol
+    assert rel(host(dw), rdw) <= TOL_F32
+
+
+# ------------------------------------------------------------------ activation
+@pytest.mark.parametrize("M,F", [(1, 8), (513, 264), (4096, 1024)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_swiglu(M, F, dtype):
+    say(f"swiglu M={M} F={F} {dtype}")
+    tdt = DTYPES[dtype]
+    code = L.dtype_code(tdt)
+    h = _normal((M, 2 * F), 5, scale=3.0, dtype=dtype)
+    da = _normal((M, F), 6, dtype=dtype)
+    a = torch.empty(M, F, dtype=tdt, device=DEV)
+    dh = torch.empty(M, 2 * F, dtype=tdt, device=DEV)
+    hd = dev(h, tdt)
+    L.moe_act_fwd(hd, M, F, code, a)
+    L.moe_act_bwd(hd, dev(da, tdt), M, F, code, dh)
+    torch.cuda.synchronize()
+    tol = TOL_ONE_ROUNDING if dtype == "bf16" else TOL_F32
+    assert rel(host(a), O.swiglu(h)) <= tol
+    assert rel(host(dh), O.swiglu_backward(h, da)) <= tol
+
+
+# ------------------------------------------------------------------ grouped GEMM
+def _groups(M, E, pattern, seed):
+    g = np.random.default_rng(seed)
+    if pattern == "uniform":
+        c = np.full(E, M // E)
+        c[: M - c.sum()] += 1
+    elif pattern == "random":
+        c = g.multinomial(M, np.ones(E) / E)
+    elif pattern == "empty":
+        c = g.multinomial(M, np.ones(E) / E)
+        c[E // 2] += c[0]
+        c[0] = 0
+    elif pattern == "one":
+        c = np.zeros(E, dtype=np.int64)
+        c[E - 1] = M
+    elif pattern == "skew":
+        p = 1.0 / np.arange(1, E + 1) ** 1.2
+        c = g.multinomial(M, p / p.sum())
+    else:
+        raise ValueError(pattern)
+    off = np.zeros(E + 1, dtype=np.int32)
+    off[1:] = np.cumsum(c)
+    return off
+
+
+GEMM_CASES = [
+    # M, K, N, E, pattern
+    (1000, 256, 384, 5, "empty"),        # 128x128 tiles, ragged rows, empty group
+    (16384, 256, 2048, 8, "random"),     # 256x256 tiles
+    (300, 512, 768, 40, "random"),       # small groups: 64x256 tiles
+    (2048, 512, 64, 1, "uniform"),       # router shape: 64x64 tiles
+    (4096, 200, 264, 3, "skew"),         # K, N not multiples of 64
+    (777, 64, 128, 4, "one"),            # every row in the last group
+    (333, 12, 20, 3, "random"),          # K, N not multiples of 8 -> FMA kernel
+]
+
+
+def _gemm_inputs(M, K, N, E, pattern, seed=0):
+    off = _groups(M, E, pattern, seed)
+    a = _normal((M, K), seed + 1)
+    b = _normal((E, K, N), seed + 2, scale=0.05)
+    dc = _normal((M, N), seed + 3)
+    return off, a, b, dc
+
+
+@pytest.mark.parametrize("M,K,N,E,pattern", GEMM_CASES)
+def test_grouped_gemm_bf16(M, K, N, E, pattern):
+    say(f"grouped_gemm bf16 M={M} K={K} N={N} E={E} {pattern}")
+    off, a, b, dc = _gemm_inputs(M, K, N, E, pattern)
+    bf, code = torch.bfloat16, L.MOE_BF16
+    ad, bd, dcd, offd = dev(a, bf), dev(b, bf), dev(dc, bf), dev(off)
+    ref_c = O.grouped_matmul(a, b, off)
+    rows = slice(0, int(off[-1]))
+    # forward, fp32 and bf16 outputs
+    c32 = torch.zeros(M, N, dtype=torch.float32, device=DEV)
+    L.moe_grouped_gemm_fwd(ad, bd, offd, M, K, N, E, code, c32, L.MOE_F32)
+    c16 = torch.zeros(M, N, dtype=bf, device=DEV)
+    L.moe_grouped_gemm_fwd(ad, bd, offd, M, K, N, E, code, c16, code)
+    torch.cuda.synchronize()
+    assert rel(host(c32)[rows], ref_c[rows]) <= TOL_F32
+    assert rel(host(c16)[rows], ref_c[rows]) <= TOL_ONE_ROUNDING
+    # backward: da (with and without addend), db (fp32)
+    ref_da, ref_db = O.grouped_matmul_backward(a, b, dc, off)
+    add = _normal((M, K), 9)
+    nb = L.moe_grouped_gemm_workspace_size(M, K, N, E, code)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=DEV)
+    da = torch.zeros(M, K, dtype=bf, device=DEV)
+    db = torch.full((E, K, N), 7.0, dtype=torch.float32, device=DEV)
+    L.moe_grouped_gemm_bwd(ad, bd, dcd, offd, M, K, N, E, code, da, None, db, ws, nb)
+    torch.cuda.synchronize()
+    assert rel(host(da)[rows], ref_da[rows]) <= TOL_ONE_ROUNDING
+    assert rel(host(db), ref_db) <= TOL_F32
+    for e in range(E):  # empty groups get exactly zero
+        if off[e + 1] == off[e]:
+            assert not host(db)[e].any()
+    L.moe_grouped_gemm_bwd(ad, bd, dcd, offd, M, K, N, E, code, da, dev(add, bf), None, ws, nb)
+    torch.cuda.synchronize()
+    assert rel(host(da)[rows], (ref_da + add)[rows]) <= TOL_ONE_ROUNDING
+
+
+@pytest.mark.parametrize("M,K,N,E,pattern", [(1000, 256, 384, 5, "empty"), (129, 36, 20, 3, "random")])
+def test_grouped_gemm_fp32(M, K, N, E, pattern):
+    say(f"grouped_gemm fp32 M={M} K={K} N={N} E={E} {pattern}")
+    off = _groups(M, E, pattern, 1)
+    a = _normal((M, K), 1, dtype="fp32")
+    b = _normal((E, K, N), 2, scale=0.05, dtype="fp32")
+    dc = _normal((M, N), 3, dtype="fp32")
+    f32 = torch.float32
+    ad, bd, dcd, offd = dev(a, f32), dev(b, f32), dev(dc, f32), dev(off)
+    c = torch.zeros(M, N, dtype=f32, device=DEV)
+    L.moe_grouped_gemm_fwd(ad, bd, offd, M, K, N, E, L.MOE_F32, c, L.MOE_F32)
+    da = torch.zeros(M, K, dtype=f32, device=DEV)
+    db = torch.zeros(E, K, N, dtype=f32, device=DEV)
+    L.moe_grouped_gemm_bwd(ad, bd, dcd, offd, M, K, N, E, L.MOE_F32, da, None, db)
+    torch.cuda.synchronize()
+    rows = slice(0, int(off[-1]))
+    assert rel(host(c)[rows], O.grouped_matmul(a, b, off)[rows]) <= TOL_F32
+    rda, rdb = O.grouped_matmul_backward(a, b, dc, off)
+    assert rel(host(da)[rows], rda[rows]) <= TOL_F32
+    assert rel(host(db), rdb) <= TOL_F32
+
+
+def test_grouped_gemm_split_weight_grad():
+    """One group with many rows and few output tiles: the weight gradient is
+    reduced in row slices (split partials in the workspace), then summed."""
+    M, K, N, E = 8192, 512, 64, 1
+    say("grouped_gemm split-reduction weight gradient")
+    off = np.array([0, M], dtype=np.int32)
+    a = _normal((M, K), 11)
+    dc = _normal((M, N), 12)
+    nb = L.moe_grouped_gemm_workspace_size(M, K, N, E, L.MOE_BF16)
+    assert nb > 0
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    db = torch.zeros(E, K, N, dtype=torch.float32, device=DEV)
+    b = _normal((E, K, N), 13, scale=0.05)
+    L.moe_grouped_gemm_bwd(dev(a, torch.bfloat16), dev(b, torch.bfloat16),
+                           dev(dc, torch.bfloat16), dev(off), M, K, N, E, L.MOE_BF16,
+                           None, None, db, ws, nb)
+    torch.cuda.synchronize()
+    _, rdb = O.grouped_matmul_backward(a, b, dc, off)
+    assert rel(host(db), rdb) <= TOL_F32

@@ -1,0 +1,138 @@
+"""GPU parity: expert selection (forward and backward) and token counting /
+index generation against the CPU oracle.  Integers bit-exact; float32 gate
+weights, probabilities and logit gradients within 1e-5 relative Frobenius."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from moe_inputs import random_topk_ids
+from tests._gpu import DEV, TOL_BF16, TOL_F32, dev, host, rel, say
+
+pytestmark = pytest.mark.gpu
+
+L = None
+
+
+@pytest.fixture(autouse=True)
+def _native_lib():
+    """The HIP library; importing it raises if it is not built (no fallback)."""
+    global L
+    import mixture_experts_layer_gating_amd._lib as lib
+    L = lib
+
+
+def _logits(T, E, seed, ties):
+    g = np.random.default_rng(seed)
+    if ties:
+        return g.integers(-2, 3, size=(T, E)).astype(np.float32)
+    return (g.standard_normal((T, E)) * 2.0).astype(np.float32)
+
+
+def _run_route(logits, k, bias=None, forced=None, renorm=False):
+    T, E = logits.shape
+    idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    p = torch.empty(T, E, dtype=torch.float32, device=DEV)
+    L.moe_route_topk(dev(logits), None if bias is None else dev(bias), T, E, k, renorm,
+                     None if forced is None else dev(forced), idx, w, p)
+    torch.cuda.synchronize()
+    return host(idx), host(w), host(p)
+
+
+ROUTE_CASES = [(1, 1, 1), (7, 3, 2), (513, 8, 2), (8192, 64, 8), (300, 65, 8), (128, 128, 8),
+               (512, 256, 8), (64, 1024, 32), (100, 200, 1), (33, 16, 16)]
+
+
+@pytest.mark.parametrize("T,E,k", ROUTE_CASES)
+@pytest.mark.parametrize("ties", [False, True])
+def test_route_topk(T, E, k, ties):
+    say(f"route_topk T={T} E={E} k={k} ties={ties}")
+    logits = _logits(T, E, T * 31 + E + k, ties)
+    idx, w, p = _run_route(logits, k)
+    oi, ow, op = O.route(logits, k)
+    np.testing.assert_array_equal(idx, oi)
+    assert rel(w, ow) <= TOL_F32 and rel(p, op) <= TOL_F32
+    np.testing.assert_allclose(w, ow, rtol=1e-4, atol=1e-12)
+
+
+@pytest.mark.parametrize("renorm", [False, True])
+def test_route_bias_forced_renorm(renorm):
+    T, E, k = 2048, 64, 8
+    say(f"route_topk bias/forced renorm={renorm}")
+    logits = _logits(T, E, 5, False)
+    bias = (-1.2 * np.log(np.random.default_rng(6).permutation(E) + 1.0)).astype(np.float32)
+    idx, w, p = _run_route(logits, k, bias=bias, renorm=renorm)
+    oi, ow, op = O.route(logits, k, bias=bias, renorm=renorm)
+    np.testing.assert_array_equal(idx, oi)
+    assert rel(w, ow) <= TOL_F32 and rel(p, op) <= TOL_F32
+    forced = random_topk_ids(T, k, E, seed=8)
+    idx, w, p = _run_route(logits, k, bias=bias, forced=forced, renorm=renorm)
+    oi, ow, op = O.route(logits, k, bias=bias, forced_idx=forced, renorm=renorm)
+    np.testing.assert_array_equal(idx, forced)
+    assert rel(w, ow) <= TOL_F32
+
+
+@pytest.mark.parametrize("T,E,k", [(7, 3, 2), (1000, 64, 8), (300, 256, 8), (50, 1024, 32)])
+@pytest.mark.parametrize("renorm", [False, True])
+def test_route_topk_bwd(T, E, k, renorm):
+    say(f"route_topk_bwd T={T} E={E} k={k} renorm={renorm}")
+    logits = _logits(T, E, 17 + E, False)
+    oi, ow, op = O.route(logits, k, renorm=renorm)
+    dw = np.random.default_rng(3).standard_normal((T, k)).astype(np.float32)
+    ref = O.gate_backward(op, oi, dw, renorm=renorm)
+    probs = dev(op.astype(np.float32))
+    for dt, tol in ((torch.float32, TOL_F32), (torch.bfloat16, TOL_BF16)):
+        out = torch.empty(T, E, dtype=dt, device=DEV)
+        L.moe_route_topk_bwd(probs, dev(oi), dev(dw), T, E, k, renorm, out, L.dtype_code(dt))
+        torch.cuda.synchronize()
+        assert rel(host(out), ref) <= tol, (dt, rel(host(out), ref))
+
+
+# ------------------------------------------------------------------ counting / indices
+def _run_count_index(ids, E):
+    T, k = ids.shape
+    Tk = T * k
+    counts = torch.empty(E, dtype=torch.int32, device=DEV)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    dest = torch.empty(Tk, dtype=torch.int32, device=DEV)
+    src = torch.empty(Tk, dtype=torch.int32, device=DEV)
+    nb = L.moe_count_index_workspace_size(T, k, E)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    L.moe_count_index(dev(ids), T, k, E, counts, offsets, dest, src, ws, nb)
+    torch.cuda.synchronize()
+    return host(counts), host(offsets), host(dest), host(src)
+
+
+def _check_ci(ids, E):
+    got = _run_count_index(ids, E)
+    want = O.build_index(ids, E)
+    for name, g, w in zip(("counts", "offsets", "dest", "src"), got, want):
+        np.testing.assert_array_equal(g, w, err_msg=name)
+    again = _run_count_index(ids, E)
+    for g, a in zip(got, again):
+        np.testing.assert_array_equal(g, a)
+
+
+CI_CASES = [(1, 1, 1), (7, 2, 3), (64, 8, 64), (513, 2, 8), (4096, 1, 1), (8192, 8, 64),
+            (16384, 8, 128), (512, 8, 256), (1000, 32, 1024), (3000, 4, 5), (4097, 1, 2)]
+
+
+@pytest.mark.parametrize("T,k,E", CI_CASES)
+def test_count_index_random(T, k, E):
+    say(f"count_index T={T} k={k} E={E}")
+    _check_ci(random_topk_ids(T, k, E, seed=T + k + E), E)
+
+
+def test_count_index_skewed_and_empty():
+    say("count_index skewed / empty experts")
+    g = np.random.default_rng(1)
+    T, k, E = 8192, 8, 64
+    # Gumbel top-k on log-Zipf weights: distinct experts, heavily skewed.
+    logw = -1.2 * np.log(np.arange(1, E + 1))
+    keys = logw[None, :] * 4 + g.gumbel(size=(T, E))
+    ids = np.argsort(-keys, axis=1)[:, :k].astype(np.int32)
+    _check_ci(ids, E)
+    # All slots on one expert; most experts empty.
+    _check_ci(np.full((5000, 1), 7, dtype=np.int32), 1024)
+    _check_ci(np.full((3, 1), 0, dtype=np.int32), 1)
