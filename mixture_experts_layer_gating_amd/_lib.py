@@ -33,6 +33,7 @@ SYMBOLS = (
     "moe_last_error", "moe_version", "moe_route_topk", "moe_route_topk_bwd",
     "moe_count_index_workspace_size", "moe_count_index", "moe_permute",
     "moe_unpermute", "moe_unpermute_bwd", "moe_grouped_gemm_workspace_size",
+    "moe_grouped_gemm_plan",
     "moe_grouped_gemm_fwd", "moe_grouped_gemm_bwd", "moe_act_fwd", "moe_act_bwd",
 )
 
@@ -90,6 +91,7 @@ _SIG = {
     "moe_unpermute": ([_p, _p, _p, _i, _i, _i, _i, _p, _p], _i),
     "moe_unpermute_bwd": ([_p, _p, _p, _p, _i, _i, _i, _i, _p, _p, _p], _i),
     "moe_grouped_gemm_workspace_size": ([_i, _i, _i, _i, _i], _z),
+    "moe_grouped_gemm_plan": ([_i, _i, _i, _i, _i, _i, _p, _p, _p, _p], _i),
     "moe_grouped_gemm_fwd": ([_p, _p, _p, _i, _i, _i, _i, _i, _p, _i, _p, _z, _p], _i),
     "moe_grouped_gemm_bwd": ([_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _z, _p], _i),
     "moe_act_fwd": ([_p, _i, _i, _i, _p, _p], _i),
@@ -190,6 +192,14 @@ def moe_unpermute_bwd(dy, yp, dest, w, T, k, d, dtype, dyp, dw, stream=None):
 
 def moe_grouped_gemm_workspace_size(M, K, N, E, dtype):
     return int(_lib.moe_grouped_gemm_workspace_size(M, K, N, E, dtype))
+
+
+def moe_grouped_gemm_plan(product, M, K, N, E, dtype):
+    """Returns dict(tile_m, tile_n, split, mfma) chosen for this shape."""
+    vals = [ctypes.c_int() for _ in range(4)]
+    _check(_lib.moe_grouped_gemm_plan(product, M, K, N, E, dtype,
+                                      *[ctypes.byref(v) for v in vals]))
+    return dict(zip(("tile_m", "tile_n", "split", "mfma"), (v.value for v in vals)))
 
 
 def moe_grouped_gemm_fwd(a, b, offsets, M, K, N, E, ab_dtype, c, c_dtype, ws=None, ws_bytes=0,

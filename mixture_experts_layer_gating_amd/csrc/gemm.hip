@@ -147,118 +147,195 @@ __device__ bool resolve_tile(const GemmArgs& p, int* sh, TileInfo& t) {
 }
 
 // ------------------------------------------------------------------ MFMA path
-constexpr int kBK = 64;        // reduction step per LDS stage
-constexpr int kThreads = 256;  // 4 waves
+// Tiles of BM x BN outputs, reduction in steps of kBK = 32, kStages = 4 LDS
+// stages.  Operand tiles go from global memory straight into LDS
+// (buffer_load_dwordx4 ... lds: each wave instruction fills 1 KB of LDS, lane
+// i writing bytes [16 i, 16 i + 16)); the LDS layout is chosen through each
+// lane's source address.  Out-of-range elements come back as zeros from the
+// buffer descriptor's range check, so the main loop has no branches.
+//
+// LDS layouts (bf16):
+//   k-contiguous operand: [O][32], 64 B per row; 16-byte chunk c of row r is
+//     stored at chunk c ^ ((r >> 2) & 3).  MFMA fragments (8 consecutive k of
+//     one row) are read with ds_read_b128; 16 consecutive rows at one chunk
+//     cover all 64 banks.
+//   k-strided operand (the reduction index is not contiguous in memory): the
+//     tile is stored as it lies in memory, [32][O] (k rows of O contiguous
+//     elements); 16-byte unit u of row k is stored at u ^ swz_t(k).  Fragments
+//     are read with two ds_read_b64_tr_b16: within each 16 lanes, lane s
+//     reads 4 elements of row k0 + s/4 at column n0 + 4 (s % 4), and the
+//     instruction returns to lane s the 4 consecutive-k elements of column
+//     n0 + s -- the MFMA operand layout.
+constexpr int kBK = 32;
+constexpr int kStages = 4;
+constexpr int kThreads = 256;           // 4 waves, 2 x 2 over the tile
+constexpr unsigned kOOB = 0x80000000u;  // buffer offset that is always out of range
 
-__device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
-  return *reinterpret_cast<const u32x4*>(p);
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long long bytes) {
+  const int n = bytes > 0x7ffffff0LL ? 0x7ffffff0 : static_cast<int>(bytes < 0 ? 0 : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
 
-// Operand descriptor: element (o, r) of the tile lives at
-//   direct:     base + o_abs * ld + r_abs    (r contiguous)
-//   transposed: base + r_abs * ld + o_abs    (o contiguous)
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+__device__ __forceinline__ int swz_c(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+
+template <int O>
+__device__ __forceinline__ int swz_t(int k) {
+  // O >= 128: a row spans >= 16 units (all banks), rows k..k+3 are spread by
+  // XOR-ing the unit with 4 (k % 4).  O == 64: rows of 8 units alternate bank
+  // halves, so only (k / 2) % 2 is needed.
+  if constexpr (O >= 128)
+    return 4 * (k & 3);
+  else
+    return 4 * ((k >> 1) & 1);
+}
+
+// Operand descriptor: element (o, r) lives at
+//   k-contiguous: base + o * ld + r           (o from 0 = the tile's first row)
+//   k-strided:    base + (r - r_lo) * ld + o  (o from 0 = the tile's first column)
 struct Operand {
   const uint16_t* base;
   long long ld;
-  int o0;    // absolute o of tile row 0
-  int olim;  // o_abs < olim is valid
+  int o_valid;  // number of valid o from the tile's first one
 };
 
-// Direct operand: thread handles O/32 chunks of 16 bytes (8 reduction elements).
-template <int O>
-struct DirectLoader {
-  static constexpr int kRegs = O * (kBK / 8) / kThreads;
-  u32x4 v[kRegs];
+// One operand of one stage: O x kBK elements = O / 16 KB, i.e. O / 16 wave
+// instructions shared by the NW waves of the workgroup.
+template <bool STRIDED, int O, int NW>
+struct DmaLoader {
+  static constexpr int kTotal = O / 16;
+  static constexpr int kPerWave = kTotal >= NW ? kTotal / NW : 1;
+  static_assert(kTotal % NW == 0 || kTotal < NW, "chunks must split evenly over waves");
+  __amdgpu_buffer_rsrc_t rsrc;
+  unsigned voff[kPerWave];  // byte offset at reduction step 0
+  int lds_off[kPerWave];    // element offset in the stage tile (wave-uniform)
+  int cofs[kPerWave];       // k-contiguous: first reduction element of this lane's chunk
+  bool ok_o[kPerWave];
+  unsigned step;            // bytes per reduction step of kBK
+  int r_hi, r_lo;
 
-  __device__ void load(const Operand& op, int r0, int r_hi) {
+  __device__ void init(const Operand& op, int r_lo_, int r_hi_) {
+    r_lo = r_lo_;
+    r_hi = r_hi_;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
 #pragma unroll
-    for (int q = 0; q < kRegs; ++q) {
-      const int c = threadIdx.x + q * kThreads;
-      const int o = c >> 3, rc = c & 7;
-      const int oa = op.o0 + o;
-      const int ra = r0 + rc * 8;
-      if (oa < op.olim && ra + 8 <= r_hi)
-        v[q] = ldg16(op.base + static_cast<long long>(oa) * op.ld + ra);
-      else
-        v[q] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ void store(uint16_t* lds) const {
-#pragma unroll
-    for (int q = 0; q < kRegs; ++q) {
-      const int c = threadIdx.x + q * kThreads;
-      const int o = c >> 3, rc = c & 7;
-      *reinterpret_cast<u32x4*>(lds + o * kBK + ((rc ^ (o & 7)) << 3)) = v[q];
-    }
-  }
-};
-
-// Transposed operand: 8x8 blocks (8 reduction rows x 8 contiguous o), one per
-// participating thread; lanes 8i..8i+7 share o-block and take the 8
-// reduction blocks, so each global load instruction reads 8 rows x 128 B and
-// each LDS write hits 8 distinct 16-byte chunks of one row.
-template <int O>
-struct TransLoader {
-  static constexpr int kBlocks = O * kBK / 64;  // 8x8 blocks per tile
-  static_assert(kBlocks <= kThreads, "one block per thread at most");
-  u32x4 v[8];
-
-  __device__ void load(const Operand& op, int r0, int r_hi) {
-    const int b = threadIdx.x;
-    if (b >= kBlocks) return;
-    const int ob = b >> 3, rb = b & 7;
-    const int oa = op.o0 + ob * 8;
-    const bool ovalid = oa + 8 <= op.olim;
-#pragma unroll
-    for (int ii = 0; ii < 8; ++ii) {
-      const int ra = r0 + rb * 8 + ii;
-      if (ovalid && ra < r_hi)
-        v[ii] = ldg16(op.base + static_cast<long long>(ra) * op.ld + oa);
-      else
-        v[ii] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ void store(uint16_t* lds) const {
-    const int b = threadIdx.x;
-    if (b >= kBlocks) return;
-    const int ob = b >> 3, rb = b & 7;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int q = jj >> 1;
-      u32x4 w;
-#pragma unroll
-      for (int p2 = 0; p2 < 4; ++p2) {
-        const uint32_t a0 = v[2 * p2][q], a1 = v[2 * p2 + 1][q];
-        w[p2] = (jj & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
+    for (int q = 0; q < kPerWave; ++q) {
+      const int cid = q * NW + w;  // 1 KB chunk of the stage tile
+      lds_off[q] = cid * 512;
+      const int pos = cid * 1024 + lane * 16;  // byte position in the tile
+      if constexpr (!STRIDED) {
+        const int row = pos / (kBK * 2);
+        const int c = swz_c(row, lane & 3);  // logical chunk for physical chunk lane % 4
+        cofs[q] = c * 8;
+        ok_o[q] = row < op.o_valid;
+        voff[q] = static_cast<unsigned>((row * op.ld + c * 8) * 2);
+      } else {
+        const int row = pos / (O * 2);
+        const int u = ((pos % (O * 2)) / 16) ^ swz_t<O>(row);
+        cofs[q] = 0;
+        ok_o[q] = u * 8 + 8 <= op.o_valid;
+        voff[q] = static_cast<unsigned>((row * op.ld + u * 8) * 2);
       }
-      const int o = ob * 8 + jj;
-      *reinterpret_cast<u32x4*>(lds + o * kBK + ((rb ^ jj) << 3)) = w;
+    }
+    if constexpr (!STRIDED) {
+      const int rows = op.o_valid < O ? (op.o_valid < 0 ? 0 : op.o_valid) : O;
+      rsrc = make_rsrc(op.base, static_cast<long long>(rows) * op.ld * 2);
+      step = kBK * 2;
+    } else {
+      rsrc = make_rsrc(op.base, static_cast<long long>(r_hi - r_lo) * op.ld * 2);
+      step = static_cast<unsigned>(kBK * op.ld * 2);
+    }
+  }
+
+  // Issue the loads of reduction step kt into stage tile `tile`.
+  __device__ __forceinline__ void issue(uint16_t* tile, int kt) const {
+    if (kTotal < NW && static_cast<int>(threadIdx.x / kWave) >= kTotal) return;
+#pragma unroll
+    for (int q = 0; q < kPerWave; ++q) {
+      bool ok = ok_o[q];
+      if constexpr (!STRIDED) ok = ok && (r_lo + kt * kBK + cofs[q] + 8 <= r_hi);
+      const unsigned off = ok ? voff[q] + static_cast<unsigned>(kt) * step : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(tile + lds_off[q]), 16, off,
+                                               0, 0, 0);
     }
   }
 };
 
-template <bool TRANS, int O>
-struct LoaderSel {
-  using type = DirectLoader<O>;
-};
-template <int O>
-struct LoaderSel<true, O> {
-  using type = TransLoader<O>;
-};
-
-__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* lds, int row, int chunk) {
-  const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * kBK + ((chunk ^ (row & 7)) << 3));
-  return __builtin_bit_cast(bf16x8, v);
+// MFMA fragment: 8 consecutive k (16 kk .. 16 kk + 15 split by lane half) of
+// row / column `idx` of the tile.
+template <bool STRIDED, int O>
+__device__ __forceinline__ bf16x8 frag(const uint16_t* tile, int base, int kk, int lane) {
+  if constexpr (!STRIDED) {
+    const int row = base + (lane & 31);
+    const int chunk = kk * 2 + (lane >> 5);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(tile + row * kBK + (swz_c(row, chunk) << 3));
+    return __builtin_bit_cast(bf16x8, v);
+  } else {
+    const int g = lane >> 4, s = lane & 15;
+    const int col = base + 16 * (g & 1) + 4 * (s & 3);
+    const int k0 = 16 * kk + 8 * (g >> 1) + (s >> 2);
+    const int u = col >> 3, sub = col & 7;
+    const uint16_t* p0 = tile + k0 * O + ((u ^ swz_t<O>(k0)) << 3) + sub;
+    const uint16_t* p1 = tile + (k0 + 4) * O + ((u ^ swz_t<O>(k0 + 4)) << 3) + sub;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p0);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p1);
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+  }
 }
 
-template <int MODE, int BM, int BN, typename OutT>
-__global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p) {
-  constexpr bool XT = (MODE == kTN);
-  constexpr bool YT = (MODE != kNT);
-  constexpr int WM = BM / 2, WN = BN / 2;
+template <int MI, int NI>
+struct Frags {
+  bf16x8 a[MI], b[NI];
+};
+
+template <bool XS, bool YS, int BM, int BN, int WM, int WN, int MI, int NI>
+__device__ __forceinline__ void read_frags(Frags<MI, NI>& f, const uint16_t* xt,
+                                           const uint16_t* yt, int kk, int wm, int wn, int lane) {
+#pragma unroll
+  for (int i = 0; i < MI; ++i) f.a[i] = frag<XS, BM>(xt, wm * WM + i * 32, kk, lane);
+#pragma unroll
+  for (int j = 0; j < NI; ++j) f.b[j] = frag<YS, BN>(yt, wn * WN + j * 32, kk, lane);
+}
+
+template <int MI, int NI>
+__device__ __forceinline__ void mfma_step(f32x16 (&acc)[MI][NI], const Frags<MI, NI>& f) {
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+// Workgroup: WGM x WGN waves, each computing a (BM / WGM) x (BN / WGN) piece.
+template <int MODE, int BM, int BN, int WGM, int WGN, typename OutT>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p) {
+  constexpr bool XS = (MODE == kTN);  // x operand k-strided in memory
+  constexpr bool YS = (MODE != kNT);  // y operand k-strided in memory
+  constexpr int NW = WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int MI = WM / 32, NI = WN / 32;
-  constexpr int STAGE = (BM + BN) * kBK;  // bf16 elements per stage
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+  constexpr int XE = BM * kBK, YE = BN * kBK;  // elements per stage tile
+  // DMA instructions per thread per stage
+  constexpr int LOADS = DmaLoader<XS, BM, NW>::kPerWave + DmaLoader<YS, BN, NW>::kPerWave;
+  // One array per stage: the compiler then tracks each stage's loads
+  // separately and waits only for the ones a read depends on.
+  __shared__ __attribute__((aligned(1024))) uint16_t st0[XE + YE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st1[XE + YE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st2[XE + YE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st3[XE + YE];
   __shared__ int sh[4];
 
   TileInfo t;
@@ -268,22 +345,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p) {
 
   Operand xo, yo;
   if constexpr (MODE == kNN) {
-    xo = {static_cast<const uint16_t*>(p.x), p.K, t.i0, t.g1};
-    yo = {static_cast<const uint16_t*>(p.y) + t.e * KN, p.N, j0, p.N};
+    xo = {static_cast<const uint16_t*>(p.x) + static_cast<long long>(t.i0) * p.K, p.K,
+          t.g1 - t.i0};
+    yo = {static_cast<const uint16_t*>(p.y) + t.e * KN + j0, p.N, p.N - j0};
   } else if constexpr (MODE == kNT) {
-    xo = {static_cast<const uint16_t*>(p.x), p.N, t.i0, t.g1};
-    yo = {static_cast<const uint16_t*>(p.y) + t.e * KN, p.N, j0, p.K};
+    xo = {static_cast<const uint16_t*>(p.x) + static_cast<long long>(t.i0) * p.N, p.N,
+          t.g1 - t.i0};
+    yo = {static_cast<const uint16_t*>(p.y) + t.e * KN + static_cast<long long>(j0) * p.N, p.N,
+          p.K - j0};
   } else {
-    xo = {static_cast<const uint16_t*>(p.x), p.K, t.i0, p.K};
-    yo = {static_cast<const uint16_t*>(p.y), p.N, j0, p.N};
+    xo = {static_cast<const uint16_t*>(p.x) + static_cast<long long>(t.r_lo) * p.K + t.i0, p.K,
+          p.K - t.i0};
+    yo = {static_cast<const uint16_t*>(p.y) + static_cast<long long>(t.r_lo) * p.N + j0, p.N,
+          p.N - j0};
   }
-
-  typename LoaderSel<XT, BM>::type xl;
-  typename LoaderSel<YT, BN>::type yl;
+  DmaLoader<XS, BM, NW> xl;
+  DmaLoader<YS, BN, NW> yl;
+  xl.init(xo, t.r_lo, t.r_hi);
+  yl.init(yo, t.r_lo, t.r_hi);
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = wid / WGN, wn = wid % WGN;
 
   f32x16 acc[MI][NI];
 #pragma unroll
@@ -295,41 +378,39 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p) {
 
   const int nk = (t.r_hi - t.r_lo + kBK - 1) / kBK;
   if (nk > 0) {
-    xl.load(xo, t.r_lo, t.r_hi);
-    yl.load(yo, t.r_lo, t.r_hi);
-    xl.store(lds);
-    yl.store(lds + BM * kBK);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const uint16_t* cur = lds + (kt & 1) * STAGE;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        const int r0 = t.r_lo + (kt + 1) * kBK;
-        xl.load(xo, r0, t.r_hi);
-        yl.load(yo, r0, t.r_hi);
-      }
+    uint16_t* const stage[kStages] = {st0, st1, st2, st3};
+    // Prologue: reduction steps 0..2 in flight, step 0 landed everywhere.
 #pragma unroll
-      for (int kk = 0; kk < kBK / 16; ++kk) {
-        const int chunk = kk * 2 + (lane >> 5);
-        bf16x8 af[MI], bfr[NI];
-#pragma unroll
-        for (int i = 0; i < MI; ++i) af[i] = lds_frag(cur, wm * WM + i * 32 + (lane & 31), chunk);
-#pragma unroll
-        for (int j = 0; j < NI; ++j)
-          bfr[j] = lds_frag(cur + BM * kBK, wn * WN + j * 32 + (lane & 31), chunk);
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int j = 0; j < NI; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
-      if (more) {
-        uint16_t* nxt = lds + ((kt + 1) & 1) * STAGE;
-        xl.store(nxt);
-        yl.store(nxt + BM * kBK);
-      }
-      __syncthreads();
+    for (int s = 0; s < kStages - 1; ++s) {
+      xl.issue(stage[s], s);
+      yl.issue(stage[s] + XE, s);
     }
+    wait_vmcnt<2 * LOADS>();
+    __builtin_amdgcn_s_barrier();
+    Frags<MI, NI> f0, f1;
+    read_frags<XS, YS, BM, BN, WM, WN>(f0, stage[0], stage[0] + XE, 0, wm, wn, lane);
+    // Step kt (stage kt % 4):  MFMAs on k-slice 0 | read slice 1 | wait until
+    // step kt+1 has landed, barrier | load step kt+3 into the stage step kt-1
+    // used | MFMAs on slice 1 | read slice 0 of step kt+1.  Steps past the
+    // reduction range load zeros; the loop runs a multiple of 4 steps.
+    for (int kt = 0; kt < nk; kt += kStages) {
+#pragma unroll
+      for (int s = 0; s < kStages; ++s) {
+        const uint16_t* cur = stage[s];
+        uint16_t* ld_stage = stage[(s + 3) & 3];
+        const uint16_t* nxt = stage[(s + 1) & 3];
+        mfma_step(acc, f0);
+        read_frags<XS, YS, BM, BN, WM, WN>(f1, cur, cur + XE, 1, wm, wn, lane);
+        wait_vmcnt<LOADS>();
+        __builtin_amdgcn_s_barrier();
+        xl.issue(ld_stage, kt + s + 3);
+        yl.issue(ld_stage + XE, kt + s + 3);
+        mfma_step(acc, f1);
+        read_frags<XS, YS, BM, BN, WM, WN>(f0, nxt, nxt + XE, 0, wm, wn, lane);
+      }
+    }
+    // Drain the loads of the last steps before the workgroup's LDS is released.
+    wait_vmcnt<0>();
   }
 
   // Epilogue.  32x32 accumulator layout: lane l, register r holds
@@ -532,11 +613,11 @@ int pick_split(int M, int K, int N, int E) {
 
 bool mfma_ok(moe_dtype dt, int K, int N) { return dt == MOE_BF16 && K % 8 == 0 && N % 8 == 0; }
 
-template <int MODE, int BM, int BN, typename OutT>
+template <int MODE, int BM, int BN, int WGM, int WGN, typename OutT>
 void launch_mfma(GemmArgs p, long long tiles_upper, hipStream_t st) {
   const long long grid = ceil_div(tiles_upper, 8) * 8;
-  hipLaunchKernelGGL((gemm_mfma_kernel<MODE, BM, BN, OutT>), dim3(static_cast<unsigned>(grid)),
-                     dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL((gemm_mfma_kernel<MODE, BM, BN, WGM, WGN, OutT>),
+                     dim3(static_cast<unsigned>(grid)), dim3(64 * WGM * WGN), 0, st, p);
 }
 
 template <int MODE, typename OutT>
@@ -551,10 +632,10 @@ void dispatch_mfma(Cfg c, GemmArgs p, long long rows_tiles_upper_fn_M, hipStream
   } else {
     upper = (ceil_div(p.M, c.bm) + p.E) * p.ntn;
   }
-  if (c.bm == 256 && c.bn == 256) launch_mfma<MODE, 256, 256, OutT>(p, upper, st);
-  else if (c.bm == 128 && c.bn == 128) launch_mfma<MODE, 128, 128, OutT>(p, upper, st);
-  else if (c.bm == 64 && c.bn == 256) launch_mfma<MODE, 64, 256, OutT>(p, upper, st);
-  else launch_mfma<MODE, 64, 64, OutT>(p, upper, st);
+  if (c.bm == 256 && c.bn == 256) launch_mfma<MODE, 256, 256, 2, 4, OutT>(p, upper, st);
+  else if (c.bm == 128 && c.bn == 128) launch_mfma<MODE, 128, 128, 2, 2, OutT>(p, upper, st);
+  else if (c.bm == 64 && c.bn == 256) launch_mfma<MODE, 64, 256, 1, 4, OutT>(p, upper, st);
+  else launch_mfma<MODE, 64, 64, 2, 2, OutT>(p, upper, st);
 }
 
 template <int MODE, typename InT, typename OutT>
@@ -596,6 +677,33 @@ extern "C" size_t moe_grouped_gemm_workspace_size(int M, int K, int N, int E, mo
   const int s = pick_split(M, K, N, E);
   if (s <= 1) return 0;
   return static_cast<size_t>(s) * E * K * N * sizeof(float);
+}
+
+extern "C" moe_status moe_grouped_gemm_plan(int product, int M, int K, int N, int E,
+                                            moe_dtype dtype, int* tile_m, int* tile_n, int* split,
+                                            int* mfma) {
+  clear_error();
+  MOE_REQUIRE(product >= 0 && product <= 2, MOE_ERR_INVALID_ARG,
+              "moe_grouped_gemm_plan: product must be 0, 1 or 2");
+  MOE_REQUIRE(M >= 1 && K >= 1 && N >= 1 && E >= 1, MOE_ERR_INVALID_ARG,
+              "moe_grouped_gemm_plan: sizes must be >= 1");
+  MOE_REQUIRE(dtype_ok(dtype), MOE_ERR_UNSUPPORTED, "moe_grouped_gemm_plan: unknown dtype");
+  const bool m = mfma_ok(dtype, K, N);
+  Cfg c{kSimtTile, kSimtTile};
+  int s = 1;
+  if (m) {
+    if (product == 0) c = pick_row_cfg(M, E, N);
+    else if (product == 1) c = pick_row_cfg(M, E, K);
+    else {
+      c = pick_tn_cfg(K, N, E);
+      s = pick_split(M, K, N, E);
+    }
+  }
+  if (tile_m) *tile_m = c.bm;
+  if (tile_n) *tile_n = c.bn;
+  if (split) *split = s;
+  if (mfma) *mfma = m ? 1 : 0;
+  return MOE_OK;
 }
 
 extern "C" moe_status moe_grouped_gemm_fwd(const void* a, const void* b, const int32_t* offsets,

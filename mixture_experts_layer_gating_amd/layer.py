@@ -28,6 +28,7 @@ Backward of <y, dy> (the forward-plus-backward unit of [Brief, Key results]):
 """
 from __future__ import annotations
 
+import contextlib
 import dataclasses
 
 import torch
@@ -103,23 +104,38 @@ class MoELayer:
         self.gemm_ws = (torch.empty(self.gemm_ws_bytes, dtype=torch.uint8, device=dev)
                         if self.gemm_ws_bytes else None)
         self._inputs = None
+        # Optional callable name -> context manager, wrapped around every
+        # library call (used by the benchmark to bracket calls with events).
+        self.timer = None
+
+    def _span(self, name):
+        return self.timer(name) if self.timer is not None else contextlib.nullcontext()
 
     # ------------------------------------------------------------------
     def forward(self, x, wr, w1, w2, bias=None, forced_idx=None, stream=None):
         T, d, E, k, F, Tk, c = self.T, self.d, self.E, self.k, self.F, self.Tk, self.code
         s = stream
-        L.moe_grouped_gemm_fwd(x, wr, self.router_offsets, T, d, E, 1, c, self.logits,
-                               L.MOE_F32, stream=s)
-        L.moe_route_topk(self.logits, bias, T, E, k, self.renorm, forced_idx, self.idx, self.w,
-                         self.probs, stream=s)
-        L.moe_count_index(self.idx, T, k, E, self.counts, self.offsets, self.dest, self.src,
-                          self.ci_ws, self.ci_ws.numel(), stream=s)
-        L.moe_permute(x, self.src, T, k, d, c, self.xp, stream=s)
-        L.moe_grouped_gemm_fwd(self.xp, w1, self.offsets, Tk, d, 2 * F, E, c, self.h, c,
-                               stream=s)
-        L.moe_act_fwd(self.h, Tk, F, c, self.a, stream=s)
-        L.moe_grouped_gemm_fwd(self.a, w2, self.offsets, Tk, F, d, E, c, self.yp, c, stream=s)
-        L.moe_unpermute(self.yp, self.dest, self.w, T, k, d, c, self.y, stream=s)
+        with self._span("router_fwd"):
+            L.moe_grouped_gemm_fwd(x, wr, self.router_offsets, T, d, E, 1, c, self.logits,
+                                   L.MOE_F32, stream=s)
+        with self._span("route_topk"):
+            L.moe_route_topk(self.logits, bias, T, E, k, self.renorm, forced_idx, self.idx,
+                             self.w, self.probs, stream=s)
+        with self._span("count_index"):
+            L.moe_count_index(self.idx, T, k, E, self.counts, self.offsets, self.dest, self.src,
+                              self.ci_ws, self.ci_ws.numel(), stream=s)
+        with self._span("permute"):
+            L.moe_permute(x, self.src, T, k, d, c, self.xp, stream=s)
+        with self._span("gemm1_fwd"):
+            L.moe_grouped_gemm_fwd(self.xp, w1, self.offsets, Tk, d, 2 * F, E, c, self.h, c,
+                                   stream=s)
+        with self._span("act_fwd"):
+            L.moe_act_fwd(self.h, Tk, F, c, self.a, stream=s)
+        with self._span("gemm2_fwd"):
+            L.moe_grouped_gemm_fwd(self.a, w2, self.offsets, Tk, F, d, E, c, self.yp, c,
+                                   stream=s)
+        with self._span("unpermute"):
+            L.moe_unpermute(self.yp, self.dest, self.w, T, k, d, c, self.y, stream=s)
         self._inputs = (x, wr, w1, w2)
         return self.y
 
@@ -130,16 +146,32 @@ class MoELayer:
         T, d, E, k, F, Tk, c = self.T, self.d, self.E, self.k, self.F, self.Tk, self.code
         s = stream
         ws, wsb = self.gemm_ws, self.gemm_ws_bytes
-        L.moe_unpermute_bwd(dy, self.yp, self.dest, self.w, T, k, d, c, self.dyp, self.dw,
-                            stream=s)
-        L.moe_grouped_gemm_bwd(self.a, w2, self.dyp, self.offsets, Tk, F, d, E, c, self.da, None,
-                               self.dw2, ws, wsb, stream=s)
-        L.moe_act_bwd(self.h, self.da, Tk, F, c, self.dh, stream=s)
-        L.moe_grouped_gemm_bwd(self.xp, w1, self.dh, self.offsets, Tk, d, 2 * F, E, c, self.dxp,
-                               None, self.dw1, ws, wsb, stream=s)
-        L.moe_unpermute(self.dxp, self.dest, None, T, k, d, c, self.dx_e, stream=s)
-        L.moe_route_topk_bwd(self.probs, self.idx, self.dw, T, E, k, self.renorm, self.dlogits,
-                             c, stream=s)
-        L.moe_grouped_gemm_bwd(x, wr, self.dlogits, self.router_offsets, T, d, E, 1, c, self.dx,
-                               self.dx_e, self.dwr, ws, wsb, stream=s)
+        with self._span("unpermute_bwd"):
+            L.moe_unpermute_bwd(dy, self.yp, self.dest, self.w, T, k, d, c, self.dyp, self.dw,
+                                stream=s)
+        with self._span("gemm2_bwd_da"):
+            L.moe_grouped_gemm_bwd(self.a, w2, self.dyp, self.offsets, Tk, F, d, E, c, self.da,
+                                   None, None, ws, wsb, stream=s)
+        with self._span("gemm2_bwd_dw"):
+            L.moe_grouped_gemm_bwd(self.a, w2, self.dyp, self.offsets, Tk, F, d, E, c, None,
+                                   None, self.dw2, ws, wsb, stream=s)
+        with self._span("act_bwd"):
+            L.moe_act_bwd(self.h, self.da, Tk, F, c, self.dh, stream=s)
+        with self._span("gemm1_bwd_da"):
+            L.moe_grouped_gemm_bwd(self.xp, w1, self.dh, self.offsets, Tk, d, 2 * F, E, c,
+                                   self.dxp, None, None, ws, wsb, stream=s)
+        with self._span("gemm1_bwd_dw"):
+            L.moe_grouped_gemm_bwd(self.xp, w1, self.dh, self.offsets, Tk, d, 2 * F, E, c, None,
+                                   None, self.dw1, ws, wsb, stream=s)
+        with self._span("permute_bwd"):
+            L.moe_unpermute(self.dxp, self.dest, None, T, k, d, c, self.dx_e, stream=s)
+        with self._span("route_topk_bwd"):
+            L.moe_route_topk_bwd(self.probs, self.idx, self.dw, T, E, k, self.renorm,
+                                 self.dlogits, c, stream=s)
+        with self._span("router_bwd_da"):
+            L.moe_grouped_gemm_bwd(x, wr, self.dlogits, self.router_offsets, T, d, E, 1, c,
+                                   self.dx, self.dx_e, None, ws, wsb, stream=s)
+        with self._span("router_bwd_dw"):
+            L.moe_grouped_gemm_bwd(x, wr, self.dlogits, self.router_offsets, T, d, E, 1, c,
+                                   None, None, self.dwr, ws, wsb, stream=s)
         return Grads(self.dx, self.dwr, self.dw1, self.dw2)
