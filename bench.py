@@ -91,7 +91,8 @@ def kernel_name(L, call, wl, code):
     if not plan["mfma"]:
         return f"gemm_simt_kernel<{prod}, ...>"
     out = "unsigned short" if prod == 1 or (prod == 0 and call != "router_fwd") else "float"
-    return f"gemm_mfma_kernel<{prod}, {plan['tile_m']}, {plan['tile_n']}, {out}>"
+    return (f"gemm_mfma_kernel<{prod}, {plan['tile_m']}, {plan['tile_n']}, "
+            f"{plan['waves_m']}, {plan['waves_n']}, {out}>")
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -142,13 +143,92 @@ def read_traffic(kernel):
         elif cur and ":" in line:
             key, val = line.split(":", 1)
             fields[cur][key.strip()] = val.strip()
-    rec = fields.get(kernel)
+    rec = None
+    for name, r in fields.items():
+        if name.startswith(kernel.split("<")[0]) and kernel.split("<")[1] in name:
+            rec = r
     if not rec or rec.get("gemm_source_sha256") != sha:
         return None
     try:
         return float(rec["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+# ---------------------------------------------------------------- profile summaries
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_trace(directory, out, command):
+    """Text summary of a rocprofv3 --kernel-trace --stats run."""
+    rows = _csv_rows(directory, "_kernel_stats.csv")
+    lines = ["# rocprofv3 kernel statistics", "", f"command: {command}", "",
+             "| kernel | calls | avg us | min us | max us | total % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("(anonymous namespace)::", "").replace("moe::", "")
+        name = name.split("(moe::")[0].split("(char")[0].split("(float")[0].split("(int")[0]
+        name = name.split("(unsigned")[0].strip()
+        lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def summarize_pmc(fetch_dir, write_dir, out, command, command2):
+    """HBM traffic per launch of each grouped-GEMM kernel from two rocprofv3
+    --pmc passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by
+    the counter's reading on the 1 GiB device copies of --copy-probe."""
+    def per_kernel(directory, counter):
+        res = {}
+        for r in _csv_rows(directory, "_counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            res.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return res
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    gib_kib = float(1 << 20)
+    # the 1 GiB copies are the copyBuffer dispatches that write ~1 GiB
+    copies = [i for i, v in enumerate(write.get("__amd_rocclr_copyBuffer", []))
+              if abs(v - gib_kib) < 0.25 * gib_kib]
+    if not copies:
+        raise SystemExit("no 1 GiB copy dispatches found (run bench.py with --copy-probe)")
+    cf = [fetch["__amd_rocclr_copyBuffer"][i] for i in copies]
+    cw = [write["__amd_rocclr_copyBuffer"][i] for i in copies]
+    f_fetch = gib_kib / (sum(cf) / len(cf))
+    f_write = gib_kib / (sum(cw) / len(cw))
+    sha = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+    lines = ["# HBM traffic of the grouped-GEMM kernels (rocprofv3 --pmc)", "",
+             f"command (FETCH_SIZE pass): {command}",
+             f"command (WRITE_SIZE pass): {command2}",
+             "",
+             f"calibration: 1 GiB device copy reads FETCH_SIZE {sum(cf) / len(cf):.0f} KiB, "
+             f"WRITE_SIZE {sum(cw) / len(cw):.0f} KiB per dispatch",
+             f"scale factors: fetch x{f_fetch:.4f}, write x{f_write:.4f}", ""]
+    for name in sorted(fetch):
+        if "gemm_mfma_kernel" not in name or name not in write:
+            continue
+        short = name.replace("(anonymous namespace)::", "").replace("moe::", "")
+        short = short.split("(")[0].replace("void ", "").strip()
+        fk = sum(fetch[name]) / len(fetch[name])
+        wk = sum(write[name]) / len(write[name])
+        traffic = fk * 1024 * f_fetch + wk * 1024 * f_write
+        lines += [f"kernel: {short}",
+                  f"  dispatches: {len(fetch[name])}",
+                  f"  fetch_kib_per_dispatch: {fk:.1f}",
+                  f"  write_kib_per_dispatch: {wk:.1f}",
+                  f"  traffic_bytes_per_launch: {traffic:.0f}",
+                  f"  gemm_source_sha256: {sha}", ""]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 # ---------------------------------------------------------------- main
@@ -158,10 +238,25 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="olmoe")
-    ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
+                    help="tokens of the CPU-oracle sample (about 10-30 s on 16 host cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="write a text summary of a rocprofv3 --kernel-trace --stats output")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write HBM traffic per grouped-GEMM launch from two --pmc outputs")
+    ap.add_argument("--out", help="summary file to write")
+    ap.add_argument("--command", default="", help="profiled command, recorded in the summary")
+    ap.add_argument("--command2", default="", help="second profiled command (WRITE_SIZE pass)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.out, args.command)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.out, args.command,
+                      args.command2)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -198,13 +198,15 @@ size_t moe_grouped_gemm_workspace_size(int M, int K, int N, int E,
  * moe_grouped_gemm_plan -- the kernel configuration the grouped GEMM entry
  * points choose for a shape (host-only query, enqueues nothing).
  * product: 0 = forward c (moe_grouped_gemm_fwd), 1 = da, 2 = db
- * (moe_grouped_gemm_bwd).  Writes the row/column tile sizes and the number
- * of reduction slices; *mfma = 1 for the bf16 MFMA kernel, 0 for the FMA
- * kernel.  Any output pointer may be NULL.
+ * (moe_grouped_gemm_bwd).  Writes the row/column tile sizes, the wavefront
+ * grid of a workgroup (waves_m x waves_n), and the number of reduction
+ * slices; *mfma = 1 for the bf16 MFMA kernel, 0 for the FMA kernel.  Any
+ * output pointer may be NULL.
  */
 moe_status moe_grouped_gemm_plan(int product, int M, int K, int N, int E,
                                  moe_dtype dtype, int* tile_m, int* tile_n,
-                                 int* split, int* mfma);
+                                 int* waves_m, int* waves_n, int* split,
+                                 int* mfma);
 moe_status moe_grouped_gemm_fwd(const void* a, const void* b,
                                 const int32_t* offsets, int M, int K, int N,
                                 int E, moe_dtype ab_dtype, void* c,

@@ -91,7 +91,7 @@ _SIG = {
     "moe_unpermute": ([_p, _p, _p, _i, _i, _i, _i, _p, _p], _i),
     "moe_unpermute_bwd": ([_p, _p, _p, _p, _i, _i, _i, _i, _p, _p, _p], _i),
     "moe_grouped_gemm_workspace_size": ([_i, _i, _i, _i, _i], _z),
-    "moe_grouped_gemm_plan": ([_i, _i, _i, _i, _i, _i, _p, _p, _p, _p], _i),
+    "moe_grouped_gemm_plan": ([_i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p], _i),
     "moe_grouped_gemm_fwd": ([_p, _p, _p, _i, _i, _i, _i, _i, _p, _i, _p, _z, _p], _i),
     "moe_grouped_gemm_bwd": ([_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _z, _p], _i),
     "moe_act_fwd": ([_p, _i, _i, _i, _p, _p], _i),
@@ -195,11 +195,13 @@ def moe_grouped_gemm_workspace_size(M, K, N, E, dtype):
 
 
 def moe_grouped_gemm_plan(product, M, K, N, E, dtype):
-    """Returns dict(tile_m, tile_n, split, mfma) chosen for this shape."""
-    vals = [ctypes.c_int() for _ in range(4)]
+    """Returns dict(tile_m, tile_n, waves_m, waves_n, split, mfma) chosen for
+    this shape."""
+    keys = ("tile_m", "tile_n", "waves_m", "waves_n", "split", "mfma")
+    vals = [ctypes.c_int() for _ in keys]
     _check(_lib.moe_grouped_gemm_plan(product, M, K, N, E, dtype,
                                       *[ctypes.byref(v) for v in vals]))
-    return dict(zip(("tile_m", "tile_n", "split", "mfma"), (v.value for v in vals)))
+    return dict(zip(keys, (v.value for v in vals)))
 
 
 def moe_grouped_gemm_fwd(a, b, offsets, M, K, N, E, ab_dtype, c, c_dtype, ws=None, ws_bytes=0,

@@ -611,6 +611,17 @@ int pick_split(int M, int K, int N, int E) {
   return static_cast<int>(s < 1 ? 1 : s);
 }
 
+// Wavefront grid of the MFMA workgroup for each tile shape (matches the
+// instantiations launched by dispatch_mfma).
+struct Waves {
+  int m, n;
+};
+Waves waves_of(Cfg c) {
+  if (c.bm == 256 && c.bn == 256) return {2, 4};
+  if (c.bm == 64 && c.bn == 256) return {1, 4};
+  return {2, 2};
+}
+
 bool mfma_ok(moe_dtype dt, int K, int N) { return dt == MOE_BF16 && K % 8 == 0 && N % 8 == 0; }
 
 template <int MODE, int BM, int BN, int WGM, int WGN, typename OutT>
@@ -621,8 +632,7 @@ void launch_mfma(GemmArgs p, long long tiles_upper, hipStream_t st) {
 }
 
 template <int MODE, typename OutT>
-void dispatch_mfma(Cfg c, GemmArgs p, long long rows_tiles_upper_fn_M, hipStream_t st) {
-  (void)rows_tiles_upper_fn_M;
+void dispatch_mfma(Cfg c, GemmArgs p, hipStream_t st) {
   const int ncols = (MODE == kNN) ? p.N : (MODE == kNT ? p.K : p.N);
   p.ntn = static_cast<int>(ceil_div(ncols, c.bn));
   long long upper;
@@ -680,8 +690,8 @@ extern "C" size_t moe_grouped_gemm_workspace_size(int M, int K, int N, int E, mo
 }
 
 extern "C" moe_status moe_grouped_gemm_plan(int product, int M, int K, int N, int E,
-                                            moe_dtype dtype, int* tile_m, int* tile_n, int* split,
-                                            int* mfma) {
+                                            moe_dtype dtype, int* tile_m, int* tile_n,
+                                            int* waves_m, int* waves_n, int* split, int* mfma) {
   clear_error();
   MOE_REQUIRE(product >= 0 && product <= 2, MOE_ERR_INVALID_ARG,
               "moe_grouped_gemm_plan: product must be 0, 1 or 2");
@@ -699,8 +709,16 @@ extern "C" moe_status moe_grouped_gemm_plan(int product, int M, int K, int N, in
       s = pick_split(M, K, N, E);
     }
   }
+  int wgm = 0, wgn = 0;
+  if (m) {
+    const Waves w = waves_of(c);
+    wgm = w.m;
+    wgn = w.n;
+  }
   if (tile_m) *tile_m = c.bm;
   if (tile_n) *tile_n = c.bn;
+  if (waves_m) *waves_m = wgm;
+  if (waves_n) *waves_n = wgn;
   if (split) *split = s;
   if (mfma) *mfma = m ? 1 : 0;
   return MOE_OK;
@@ -722,8 +740,8 @@ extern "C" moe_status moe_grouped_gemm_fwd(const void* a, const void* b, const i
   hipStream_t st = as_stream(stream);
   if (mfma_ok(ab_dtype, K, N)) {
     const Cfg cfg = pick_row_cfg(M, E, N);
-    if (c_dtype == MOE_BF16) dispatch_mfma<kNN, uint16_t>(cfg, p, 0, st);
-    else dispatch_mfma<kNN, float>(cfg, p, 0, st);
+    if (c_dtype == MOE_BF16) dispatch_mfma<kNN, uint16_t>(cfg, p, st);
+    else dispatch_mfma<kNN, float>(cfg, p, st);
   } else if (ab_dtype == MOE_BF16) {
     if (c_dtype == MOE_BF16) launch_simt<kNN, uint16_t, uint16_t>(p, st);
     else launch_simt<kNN, uint16_t, float>(p, st);
@@ -761,7 +779,7 @@ extern "C" moe_status moe_grouped_gemm_bwd(const void* a, const void* b, const v
   if (da) {
     GemmArgs p{dc, b, da_add, da, offsets, M, K, N, E, 0, 0, 1};
     if (use_mfma) {
-      dispatch_mfma<kNT, uint16_t>(pick_row_cfg(M, E, K), p, 0, st);
+      dispatch_mfma<kNT, uint16_t>(pick_row_cfg(M, E, K), p, st);
     } else if (dtype == MOE_BF16) {
       launch_simt<kNT, uint16_t, uint16_t>(p, st);
     } else {
@@ -773,7 +791,7 @@ extern "C" moe_status moe_grouped_gemm_bwd(const void* a, const void* b, const v
     if (use_mfma) {
       GemmArgs p{a, dc, nullptr, split > 1 ? ws : static_cast<void*>(db), offsets, M, K, N, E,
                  0, 0, split};
-      dispatch_mfma<kTN, float>(pick_tn_cfg(K, N, E), p, 0, st);
+      dispatch_mfma<kTN, float>(pick_tn_cfg(K, N, E), p, st);
       if (moe_status s = check_launch("moe_grouped_gemm_bwd/db")) return s;
       if (split > 1) {
         const long long n = static_cast<long long>(E) * K * N;
