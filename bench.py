@@ -96,9 +96,10 @@ def kernel_name(L, call, wl, code):
 
 
 # ---------------------------------------------------------------- CPU baseline
-def cpu_baseline(inp, tokens):
+def cpu_baseline(inp, tokens, reps=2):
     """Time the CPU oracle (float64 NumPy, as it stands) on the first
-    ``tokens`` tokens of the same workload: forward + backward."""
+    ``tokens`` tokens of the same workload: forward + backward, ``reps``
+    times; reports the mean rate."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
 
@@ -114,15 +115,18 @@ def cpu_baseline(inp, tokens):
         info = threadpool_info()
         used = max([i.get("num_threads", 1) for i in info] or [1])
         x = inp.x[t]
+        forced = None if inp.forced_idx is None else inp.forced_idx[t]
         t0 = time.perf_counter()
-        fwd = O.layer_forward(x, inp.wr, inp.w1, inp.w2, wl.k, bias=inp.bias,
-                              forced_idx=None if inp.forced_idx is None else inp.forced_idx[t])
-        O.layer_backward(fwd, inp.dy[t], x, inp.wr, inp.w1, inp.w2, wl.k)
+        for _ in range(reps):
+            fwd = O.layer_forward(x, inp.wr, inp.w1, inp.w2, wl.k, bias=inp.bias,
+                                  forced_idx=forced)
+            O.layer_backward(fwd, inp.dy[t], x, inp.wr, inp.w1, inp.w2, wl.k)
+            del fwd
         dt = time.perf_counter() - t0
-    return {"value": round(tokens / dt, 3), "unit": "tokens/s", "cores": int(used),
+    return {"value": round(tokens * reps / dt, 3), "unit": "tokens/s", "cores": int(used),
             "kind": "oracle",
-            "sample": (f"first {tokens} of {wl.T} tokens of the same layer (full weights), "
-                       f"float64 NumPy forward+backward, {dt:.1f} s")}
+            "sample": (f"{tokens} of {wl.T} tokens of the same layer (full weights), "
+                       f"float64 NumPy forward+backward, {reps} passes, {dt:.1f} s")}
 
 
 # ---------------------------------------------------------------- traffic
@@ -238,8 +242,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="olmoe")
-    ap.add_argument("--cpu-tokens", type=int, default=4096,
-                    help="tokens of the CPU-oracle sample (about 10-30 s on 16 host cores)")
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens of the CPU-oracle sample (default: the whole workload; "
+                         "two passes take about 15 s on 16 host cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--summarize-trace", metavar="DIR",
@@ -391,8 +396,8 @@ def main():
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
-        log(f"[bench] cpu baseline: oracle on {args.cpu_tokens} tokens")
-        out["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_tokens, wl.T))
+        log("[bench] cpu baseline: float64 oracle")
+        out["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_tokens or wl.T, wl.T))
     else:
         out["cpu_baseline"] = None
     del np
