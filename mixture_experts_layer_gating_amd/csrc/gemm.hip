@@ -301,22 +301,69 @@ struct Frags {
   bf16x8 a[MI], b[NI];
 };
 
-template <bool XS, bool YS, int BM, int BN, int WM, int WN, int MI, int NI>
+// Fragments of the first MIV 32-row blocks of this wave's rows (the rest of
+// the wave's rows are past the end of its group) and all its columns.
+template <int MIV, bool XS, bool YS, int BM, int BN, int WM, int WN, int MI, int NI>
 __device__ __forceinline__ void read_frags(Frags<MI, NI>& f, const uint16_t* xt,
                                            const uint16_t* yt, int kk, int wm, int wn, int lane) {
+  if constexpr (MIV > 0) {
 #pragma unroll
-  for (int i = 0; i < MI; ++i) f.a[i] = frag<XS, BM>(xt, wm * WM + i * 32, kk, lane);
+    for (int i = 0; i < MIV; ++i) f.a[i] = frag<XS, BM>(xt, wm * WM + i * 32, kk, lane);
 #pragma unroll
-  for (int j = 0; j < NI; ++j) f.b[j] = frag<YS, BN>(yt, wn * WN + j * 32, kk, lane);
+    for (int j = 0; j < NI; ++j) f.b[j] = frag<YS, BN>(yt, wn * WN + j * 32, kk, lane);
+  }
 }
 
-template <int MI, int NI>
+template <int MIV, int MI, int NI>
 __device__ __forceinline__ void mfma_step(f32x16 (&acc)[MI][NI], const Frags<MI, NI>& f) {
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int i = 0; i < MIV; ++i)
 #pragma unroll
     for (int j = 0; j < NI; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+// The reduction loop of one workgroup tile.  Every wave issues its share of
+// the loads and takes part in every barrier; only the MFMAs (and fragment
+// reads) of row blocks past the end of the group are left out.
+template <int MIV, bool XS, bool YS, int BM, int BN, int WM, int WN, int MI, int NI, int LOADS,
+          class XL, class YL>
+__device__ __forceinline__ void reduce_tile(f32x16 (&acc)[MI][NI], const XL& xl, const YL& yl,
+                                            uint16_t* const (&stage)[kStages], int nk, int wm,
+                                            int wn, int lane) {
+  constexpr int XE = BM * kBK;
+  // Prologue: reduction steps 0..2 in flight, step 0 landed everywhere.
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) {
+    xl.issue(stage[s], s);
+    yl.issue(stage[s] + XE, s);
+  }
+  wait_vmcnt<2 * LOADS>();
+  __builtin_amdgcn_s_barrier();
+  Frags<MI, NI> f0, f1;
+  read_frags<MIV, XS, YS, BM, BN, WM, WN>(f0, stage[0], stage[0] + XE, 0, wm, wn, lane);
+  // Step kt (stage kt % 4):  MFMAs on k-slice 0 | read slice 1 | wait until
+  // step kt+1 has landed, barrier | load step kt+3 into the stage step kt-1
+  // used | MFMAs on slice 1 | read slice 0 of step kt+1.  Steps past the
+  // reduction range load zeros; the loop runs a multiple of 4 steps.
+  for (int kt = 0; kt < nk; kt += kStages) {
+#pragma unroll
+    for (int s = 0; s < kStages; ++s) {
+      const uint16_t* cur = stage[s];
+      uint16_t* ld_stage = stage[(s + 3) & 3];
+      const uint16_t* nxt = stage[(s + 1) & 3];
+      mfma_step<MIV>(acc, f0);
+      read_frags<MIV, XS, YS, BM, BN, WM, WN>(f1, cur, cur + XE, 1, wm, wn, lane);
+      wait_vmcnt<LOADS>();
+      __builtin_amdgcn_s_barrier();
+      xl.issue(ld_stage, kt + s + 3);
+      yl.issue(ld_stage + XE, kt + s + 3);
+      mfma_step<MIV>(acc, f1);
+      read_frags<MIV, XS, YS, BM, BN, WM, WN>(f0, nxt, nxt + XE, 0, wm, wn, lane);
+    }
+  }
+  // Drain the loads of the last steps before the workgroup's LDS is released.
+  wait_vmcnt<0>();
 }
 
 // Workgroup: WGM x WGN waves, each computing a (BM / WGM) x (BN / WGN) piece.
@@ -379,38 +426,27 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
   const int nk = (t.r_hi - t.r_lo + kBK - 1) / kBK;
   if (nk > 0) {
     uint16_t* const stage[kStages] = {st0, st1, st2, st3};
-    // Prologue: reduction steps 0..2 in flight, step 0 landed everywhere.
-#pragma unroll
-    for (int s = 0; s < kStages - 1; ++s) {
-      xl.issue(stage[s], s);
-      yl.issue(stage[s] + XE, s);
+    // Row blocks of this wave that hold rows of the tile (partial last tiles
+    // of a group, or of K in the weight-gradient layout).
+    const int rows = (MODE == kTN) ? p.K - t.i0 : t.g1 - t.i0;
+    const int rem = rows - wm * WM;
+    const int miv = rem <= 0 ? 0 : (rem >= WM ? MI : (rem + 31) / 32);
+#define MOE_REDUCE(V)                                                                     \
+  reduce_tile<V, XS, YS, BM, BN, WM, WN, MI, NI, LOADS>(acc, xl, yl, stage, nk, wm, wn, lane)
+    if (miv == MI) {
+      MOE_REDUCE(MI);
+    } else if constexpr (MI == 4) {
+      if (miv == 3) MOE_REDUCE(3);
+      else if (miv == 2) MOE_REDUCE(2);
+      else if (miv == 1) MOE_REDUCE(1);
+      else MOE_REDUCE(0);
+    } else if constexpr (MI == 2) {
+      if (miv == 1) MOE_REDUCE(1);
+      else MOE_REDUCE(0);
+    } else {
+      MOE_REDUCE(0);
     }
-    wait_vmcnt<2 * LOADS>();
-    __builtin_amdgcn_s_barrier();
-    Frags<MI, NI> f0, f1;
-    read_frags<XS, YS, BM, BN, WM, WN>(f0, stage[0], stage[0] + XE, 0, wm, wn, lane);
-    // Step kt (stage kt % 4):  MFMAs on k-slice 0 | read slice 1 | wait until
-    // step kt+1 has landed, barrier | load step kt+3 into the stage step kt-1
-    // used | MFMAs on slice 1 | read slice 0 of step kt+1.  Steps past the
-    // reduction range load zeros; the loop runs a multiple of 4 steps.
-    for (int kt = 0; kt < nk; kt += kStages) {
-#pragma unroll
-      for (int s = 0; s < kStages; ++s) {
-        const uint16_t* cur = stage[s];
-        uint16_t* ld_stage = stage[(s + 3) & 3];
-        const uint16_t* nxt = stage[(s + 1) & 3];
-        mfma_step(acc, f0);
-        read_frags<XS, YS, BM, BN, WM, WN>(f1, cur, cur + XE, 1, wm, wn, lane);
-        wait_vmcnt<LOADS>();
-        __builtin_amdgcn_s_barrier();
-        xl.issue(ld_stage, kt + s + 3);
-        yl.issue(ld_stage + XE, kt + s + 3);
-        mfma_step(acc, f1);
-        read_frags<XS, YS, BM, BN, WM, WN>(f0, nxt, nxt + XE, 0, wm, wn, lane);
-      }
-    }
-    // Drain the loads of the last steps before the workgroup's LDS is released.
-    wait_vmcnt<0>();
+#undef MOE_REDUCE
   }
 
   // Epilogue.  32x32 accumulator layout: lane l, register r holds
