@@ -133,13 +133,15 @@ moe_status moe_count_index(const int32_t* topk_idx, int T, int k, int E,
                            moe_stream_t stream);
 
 /*
- * moe_permute -- gather token rows into expert-contiguous order:
+ * moe_permute -- copy token rows into expert-contiguous order:
+ * xp[dest[t*k + j], :] = x[t, :] for every slot (t, j), i.e.
  * xp[p, :] = x[src[p] / k, :].  The expert computation on the pages runs on
  * tokens grouped per expert [Brief, Core method].
- *   x [T, d], xp [T*k, d], both `dtype`.   src [T*k] int32 from
- *   moe_count_index.  Requires d % 8 == 0.  Bitwise copy.
+ *   x [T, d], xp [T*k, d], both `dtype`.   dest [T*k] int32 from
+ *   moe_count_index (a permutation of [0, T*k)).  Requires d % 8 == 0.
+ *   Bitwise copy.
  */
-moe_status moe_permute(const void* x, const int32_t* src, int T, int k, int d,
+moe_status moe_permute(const void* x, const int32_t* dest, int T, int k, int d,
                        moe_dtype dtype, void* xp, moe_stream_t stream);
 
 /*

@@ -176,8 +176,8 @@ def moe_count_index(topk_idx, T, k, E, counts, offsets, dest, src, ws, ws_bytes,
                                 _stream(stream, topk_idx)))
 
 
-def moe_permute(x, src, T, k, d, dtype, xp, stream=None):
-    _check(_lib.moe_permute(_ptr(x), _ptr(src), T, k, d, dtype, _ptr(xp), _stream(stream, x)))
+def moe_permute(x, dest, T, k, d, dtype, xp, stream=None):
+    _check(_lib.moe_permute(_ptr(x), _ptr(dest), T, k, d, dtype, _ptr(xp), _stream(stream, x)))
 
 
 def moe_unpermute(yp, dest, w, T, k, d, dtype, y, stream=None):

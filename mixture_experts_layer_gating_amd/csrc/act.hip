@@ -52,62 +52,64 @@ __device__ __forceinline__ void store_f32(T* p, const float* f) {
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.f / (1.f + expf(-z)); }
 
+// Flat 32-bit index over (row, 16-byte chunk of the gate half), one chunk per
+// thread per grid-stride step.
 template <typename T>
-__global__ __launch_bounds__(kActBlock) void act_fwd_kernel(const T* __restrict__ h, long long M,
-                                                            int F, T* __restrict__ a) {
+__global__ __launch_bounds__(kActBlock) void act_fwd_kernel(const T* __restrict__ h, int M, int F,
+                                                            T* __restrict__ a) {
   constexpr int N = Elems<T>::N;
   const int cpr = F / N;
-  const long long total = M * cpr;
-  for (long long i = blockIdx.x * static_cast<long long>(kActBlock) + threadIdx.x; i < total;
-       i += static_cast<long long>(gridDim.x) * kActBlock) {
-    const long long m = i / cpr;
-    const int c = static_cast<int>(i - m * cpr);
-    const T* hr = h + m * 2 * F;
+  const int total = M * cpr;
+  for (int i = blockIdx.x * kActBlock + threadIdx.x; i < total; i += gridDim.x * kActBlock) {
+    const int m = i / cpr, c = i - m * cpr;
+    const T* hr = h + static_cast<size_t>(m) * 2 * F + c * N;
     float g[N], u[N], o[N];
-    load_f32(hr + c * N, g);
-    load_f32(hr + F + c * N, u);
+    load_f32(hr, g);
+    load_f32(hr + F, u);
 #pragma unroll
-    for (int q = 0; q < N; ++q) o[q] = g[q] * sigmoidf_(g[q]) * u[q];
-    store_f32(a + m * F + c * N, o);
+    for (int e = 0; e < N; ++e) o[e] = g[e] * sigmoidf_(g[e]) * u[e];
+    store_f32(a + static_cast<size_t>(m) * F + c * N, o);
   }
 }
 
 template <typename T>
 __global__ __launch_bounds__(kActBlock) void act_bwd_kernel(const T* __restrict__ h,
-                                                            const T* __restrict__ da, long long M,
+                                                            const T* __restrict__ da, int M,
                                                             int F, T* __restrict__ dh) {
   constexpr int N = Elems<T>::N;
   const int cpr = F / N;
-  const long long total = M * cpr;
-  for (long long i = blockIdx.x * static_cast<long long>(kActBlock) + threadIdx.x; i < total;
-       i += static_cast<long long>(gridDim.x) * kActBlock) {
-    const long long m = i / cpr;
-    const int c = static_cast<int>(i - m * cpr);
-    const T* hr = h + m * 2 * F;
+  const int total = M * cpr;
+  for (int i = blockIdx.x * kActBlock + threadIdx.x; i < total; i += gridDim.x * kActBlock) {
+    const int m = i / cpr, c = i - m * cpr;
+    const T* hr = h + static_cast<size_t>(m) * 2 * F + c * N;
     float g[N], u[N], d[N], dg[N], du[N];
-    load_f32(hr + c * N, g);
-    load_f32(hr + F + c * N, u);
-    load_f32(da + m * F + c * N, d);
+    load_f32(hr, g);
+    load_f32(hr + F, u);
+    load_f32(da + static_cast<size_t>(m) * F + c * N, d);
 #pragma unroll
-    for (int q = 0; q < N; ++q) {
-      const float s = sigmoidf_(g[q]);
-      dg[q] = d[q] * u[q] * s * (1.f + g[q] * (1.f - s));
-      du[q] = d[q] * g[q] * s;
+    for (int e = 0; e < N; ++e) {
+      const float s = sigmoidf_(g[e]);
+      dg[e] = d[e] * u[e] * s * (1.f + g[e] * (1.f - s));
+      du[e] = d[e] * g[e] * s;
     }
-    T* dr = dh + m * 2 * F;
-    store_f32(dr + c * N, dg);
-    store_f32(dr + F + c * N, du);
+    T* dr = dh + static_cast<size_t>(m) * 2 * F + c * N;
+    store_f32(dr, dg);
+    store_f32(dr + F, du);
   }
 }
 
-int act_grid(long long items) {
-  long long b = (items + kActBlock - 1) / kActBlock;
+int act_grid(int M, int F, moe_dtype dt) {
+  // One chunk per thread, capped at 32 workgroups per compute unit.
+  const long long chunks = static_cast<long long>(M) * F * static_cast<long long>(dtype_size(dt)) / 16;
+  long long b = (chunks + kActBlock - 1) / kActBlock;
   if (b > 256LL * 32) b = 256LL * 32;
   return static_cast<int>(b < 1 ? 1 : b);
 }
 
 moe_status check_act(int M, int F, moe_dtype dt) {
   MOE_REQUIRE(M >= 1 && F >= 1, MOE_ERR_INVALID_ARG, "M and F must be >= 1");
+  MOE_REQUIRE(static_cast<long long>(M) * F < (1ll << 31), MOE_ERR_UNSUPPORTED,
+              "M*F must be < 2^31");
   MOE_REQUIRE(dtype_ok(dt), MOE_ERR_UNSUPPORTED, "unknown dtype");
   MOE_REQUIRE(F % 8 == 0, MOE_ERR_UNSUPPORTED, "F must be a multiple of 8");
   return MOE_OK;
@@ -123,14 +125,13 @@ extern "C" moe_status moe_act_fwd(const void* h, int M, int F, moe_dtype dtype, 
   clear_error();
   if (moe_status s = check_act(M, F, dtype)) return s;
   MOE_REQUIRE(h && a, MOE_ERR_INVALID_ARG, "moe_act_fwd: null pointer");
-  const long long items = static_cast<long long>(M) * F * static_cast<long long>(dtype_size(dtype)) / 16;
   if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(act_fwd_kernel<uint16_t>, dim3(act_grid(items)), dim3(kActBlock), 0,
-                       as_stream(stream), static_cast<const uint16_t*>(h), (long long)M, F,
+    hipLaunchKernelGGL(act_fwd_kernel<uint16_t>, dim3(act_grid(M, F, dtype)), dim3(kActBlock), 0,
+                       as_stream(stream), static_cast<const uint16_t*>(h), M, F,
                        static_cast<uint16_t*>(a));
   else
-    hipLaunchKernelGGL(act_fwd_kernel<float>, dim3(act_grid(items)), dim3(kActBlock), 0,
-                       as_stream(stream), static_cast<const float*>(h), (long long)M, F,
+    hipLaunchKernelGGL(act_fwd_kernel<float>, dim3(act_grid(M, F, dtype)), dim3(kActBlock), 0,
+                       as_stream(stream), static_cast<const float*>(h), M, F,
                        static_cast<float*>(a));
   return check_launch("moe_act_fwd");
 }
@@ -140,15 +141,13 @@ extern "C" moe_status moe_act_bwd(const void* h, const void* da, int M, int F, m
   clear_error();
   if (moe_status s = check_act(M, F, dtype)) return s;
   MOE_REQUIRE(h && da && dh, MOE_ERR_INVALID_ARG, "moe_act_bwd: null pointer");
-  const long long items = static_cast<long long>(M) * F * static_cast<long long>(dtype_size(dtype)) / 16;
   if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(act_bwd_kernel<uint16_t>, dim3(act_grid(items)), dim3(kActBlock), 0,
+    hipLaunchKernelGGL(act_bwd_kernel<uint16_t>, dim3(act_grid(M, F, dtype)), dim3(kActBlock), 0,
                        as_stream(stream), static_cast<const uint16_t*>(h),
-                       static_cast<const uint16_t*>(da), (long long)M, F,
-                       static_cast<uint16_t*>(dh));
+                       static_cast<const uint16_t*>(da), M, F, static_cast<uint16_t*>(dh));
   else
-    hipLaunchKernelGGL(act_bwd_kernel<float>, dim3(act_grid(items)), dim3(kActBlock), 0,
+    hipLaunchKernelGGL(act_bwd_kernel<float>, dim3(act_grid(M, F, dtype)), dim3(kActBlock), 0,
                        as_stream(stream), static_cast<const float*>(h),
-                       static_cast<const float*>(da), (long long)M, F, static_cast<float*>(dh));
+                       static_cast<const float*>(da), M, F, static_cast<float*>(dh));
   return check_launch("moe_act_bwd");
 }

@@ -59,25 +59,31 @@ struct Chunk<float> {
   }
 };
 
-// xp[p, :] = x[src[p] / k, :]; grid-stride over (row, chunk) pairs.
+// xp[dest[t*k + j], :] = x[t, :] for every slot (t, j): each token row is
+// read once and written to its k rows (the same result as gathering
+// xp[p] = x[src[p] / k]).  One workgroup per token row, threads on
+// consecutive 16-byte chunks; stores do not wait, so k of them per load keep
+// the memory system busy.
 __global__ __launch_bounds__(kMoveBlock) void permute_kernel(const char* __restrict__ x,
-                                                             const int32_t* __restrict__ src,
-                                                             long long rows, int k,
-                                                             int chunks_per_row,
+                                                             const int32_t* __restrict__ dest,
+                                                             int Tn, int k, int chunks_per_row,
                                                              char* __restrict__ xp) {
-  const long long total = rows * chunks_per_row;
   const size_t row_bytes = static_cast<size_t>(chunks_per_row) * 16;
-  for (long long i = blockIdx.x * static_cast<long long>(kMoveBlock) + threadIdx.x; i < total;
-       i += static_cast<long long>(gridDim.x) * kMoveBlock) {
-    const long long p = i / chunks_per_row;
-    const int c = static_cast<int>(i - p * chunks_per_row);
-    const int t = src[p] / k;
-    st16(xp + p * row_bytes + c * 16, ld16(x + static_cast<size_t>(t) * row_bytes + c * 16));
+  for (int t = blockIdx.x; t < Tn; t += gridDim.x) {
+    const char* in = x + static_cast<size_t>(t) * row_bytes;
+    const int32_t* drow = dest + static_cast<size_t>(t) * k;
+    for (int c = threadIdx.x; c < chunks_per_row; c += kMoveBlock) {
+      const Vec16 v = ld16(in + c * 16);
+      for (int j = 0; j < k; ++j) st16(xp + static_cast<size_t>(drow[j]) * row_bytes + c * 16, v);
+    }
   }
 }
 
+constexpr int kUnroll = 8;  // slots whose loads are issued together
+
 // y[t, :] = sum_j w[t, j] * yp[dest[t*k + j], :]  (w == nullptr -> weight 1)
-// with fp32 accumulation in increasing j.
+// with fp32 accumulation in increasing j.  One workgroup per output row; the
+// loads of up to 8 slots are issued before any of them is used.
 template <typename T>
 __global__ __launch_bounds__(kMoveBlock) void unpermute_kernel(const char* __restrict__ yp,
                                                                const int32_t* __restrict__ dest,
@@ -85,25 +91,32 @@ __global__ __launch_bounds__(kMoveBlock) void unpermute_kernel(const char* __res
                                                                int Tn, int k, int chunks_per_row,
                                                                char* __restrict__ y) {
   constexpr int N = Chunk<T>::N;
-  const long long total = static_cast<long long>(Tn) * chunks_per_row;
   const size_t row_bytes = static_cast<size_t>(chunks_per_row) * 16;
-  for (long long i = blockIdx.x * static_cast<long long>(kMoveBlock) + threadIdx.x; i < total;
-       i += static_cast<long long>(gridDim.x) * kMoveBlock) {
-    const int t = static_cast<int>(i / chunks_per_row);
-    const int c = static_cast<int>(i - static_cast<long long>(t) * chunks_per_row);
-    float acc[N];
+  for (int t = blockIdx.x; t < Tn; t += gridDim.x) {
+    const int32_t* drow = dest + static_cast<size_t>(t) * k;
+    const float* wrow = w ? w + static_cast<size_t>(t) * k : nullptr;
+    for (int c = threadIdx.x; c < chunks_per_row; c += kMoveBlock) {
+      float acc[N];
 #pragma unroll
-    for (int q = 0; q < N; ++q) acc[q] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const size_t s = static_cast<size_t>(t) * k + j;
-      const int r = dest[s];
-      const float wt = w ? w[s] : 1.f;
-      float v[N];
-      Chunk<T>::unpack(ld16(yp + static_cast<size_t>(r) * row_bytes + c * 16), v);
+      for (int q = 0; q < N; ++q) acc[q] = 0.f;
+      for (int j0 = 0; j0 < k; j0 += kUnroll) {
+        Vec16 raw[kUnroll];
 #pragma unroll
-      for (int q = 0; q < N; ++q) acc[q] = fmaf(wt, v[q], acc[q]);
+        for (int u = 0; u < kUnroll; ++u)
+          if (j0 + u < k) raw[u] = ld16(yp + static_cast<size_t>(drow[j0 + u]) * row_bytes + c * 16);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          if (j0 + u < k) {
+            const float wt = wrow ? wrow[j0 + u] : 1.f;
+            float v[N];
+            Chunk<T>::unpack(raw[u], v);
+#pragma unroll
+            for (int q = 0; q < N; ++q) acc[q] = fmaf(wt, v[q], acc[q]);
+          }
+        }
+      }
+      st16(y + static_cast<size_t>(t) * row_bytes + c * 16, Chunk<T>::pack(acc));
     }
-    st16(y + static_cast<size_t>(t) * row_bytes + c * 16, Chunk<T>::pack(acc));
   }
 }
 
@@ -120,37 +133,56 @@ __global__ __launch_bounds__(kMoveBlock) void unpermute_bwd_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
   const char* dyrow = dy + static_cast<size_t>(t) * row_bytes;
-  for (int j = 0; j < k; ++j) {
-    const size_t s = static_cast<size_t>(t) * k + j;
-    const int r = dest[s];
-    const float wt = w[s];
-    float dot = 0.f;
-    for (int c = threadIdx.x; c < chunks_per_row; c += kMoveBlock) {
-      float g[N], v[N], o[N];
-      Chunk<T>::unpack(ld16(dyrow + c * 16), g);
-      Chunk<T>::unpack(ld16(yp + static_cast<size_t>(r) * row_bytes + c * 16), v);
+  const int32_t* drow = dest + static_cast<size_t>(t) * k;
+  const float* wrow = w + static_cast<size_t>(t) * k;
+  float dot[MOE_MAX_TOPK];
 #pragma unroll
-      for (int q = 0; q < N; ++q) {
-        dot = fmaf(g[q], v[q], dot);
-        o[q] = wt * g[q];
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) dot[j] = 0.f;
+  for (int c = threadIdx.x; c < chunks_per_row; c += kMoveBlock) {
+    float g[N];
+    Chunk<T>::unpack(ld16(dyrow + c * 16), g);
+#pragma unroll
+    for (int j0 = 0; j0 < MOE_MAX_TOPK; j0 += kUnroll) {
+      if (j0 >= k) break;
+      Vec16 raw[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        if (j0 + u < k) raw[u] = ld16(yp + static_cast<size_t>(drow[j0 + u]) * row_bytes + c * 16);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        if (j0 + u < k) {
+          const float wt = wrow[j0 + u];
+          float v[N], o[N];
+          Chunk<T>::unpack(raw[u], v);
+#pragma unroll
+          for (int q = 0; q < N; ++q) {
+            dot[j0 + u] = fmaf(g[q], v[q], dot[j0 + u]);
+            o[q] = wt * g[q];
+          }
+          st16(dyp + static_cast<size_t>(drow[j0 + u]) * row_bytes + c * 16, Chunk<T>::pack(o));
+        }
       }
-      st16(dyp + static_cast<size_t>(r) * row_bytes + c * 16, Chunk<T>::pack(o));
     }
-    dot = wave_sum(dot);
-    if (lane == 0) part[wid][j] = dot;
+  }
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    if (j < k) {
+      const float v = wave_sum(dot[j]);
+      if (lane == 0) part[wid][j] = v;
+    }
   }
   __syncthreads();
   if (threadIdx.x < k) {
-    float s = 0.f;
+    float acc = 0.f;
 #pragma unroll
-    for (int q = 0; q < kMoveBlock / kWave; ++q) s += part[q][threadIdx.x];
-    dw[static_cast<size_t>(t) * k + threadIdx.x] = s;
+    for (int q = 0; q < kMoveBlock / kWave; ++q) acc += part[q][threadIdx.x];
+    dw[static_cast<size_t>(t) * k + threadIdx.x] = acc;
   }
 }
 
-int move_grid(long long work_items) {
-  // Enough blocks to cover the work, capped at 32 per compute unit (256 CUs).
-  long long b = (work_items + kMoveBlock - 1) / kMoveBlock;
+int row_grid(long long rows) {
+  // One workgroup per row, capped at 32 per compute unit (256 CUs).
+  long long b = rows;
   if (b > 256LL * 32) b = 256LL * 32;
   return static_cast<int>(b < 1 ? 1 : b);
 }
@@ -170,16 +202,14 @@ moe_status check_move(int T, int k, int d, moe_dtype dt) {
 
 using namespace moe;
 
-extern "C" moe_status moe_permute(const void* x, const int32_t* src, int T, int k, int d,
+extern "C" moe_status moe_permute(const void* x, const int32_t* dest, int T, int k, int d,
                                   moe_dtype dtype, void* xp, moe_stream_t stream) {
   clear_error();
   if (moe_status s = check_move(T, k, d, dtype)) return s;
-  MOE_REQUIRE(x && src && xp, MOE_ERR_INVALID_ARG, "moe_permute: null pointer");
+  MOE_REQUIRE(x && dest && xp, MOE_ERR_INVALID_ARG, "moe_permute: null pointer");
   const int cpr = static_cast<int>(d * dtype_size(dtype) / 16);
-  const long long rows = static_cast<long long>(T) * k;
-  hipLaunchKernelGGL(permute_kernel, dim3(move_grid(rows * cpr)), dim3(kMoveBlock), 0,
-                     as_stream(stream), static_cast<const char*>(x), src, rows, k, cpr,
-                     static_cast<char*>(xp));
+  hipLaunchKernelGGL(permute_kernel, dim3(row_grid(T)), dim3(kMoveBlock), 0, as_stream(stream),
+                     static_cast<const char*>(x), dest, T, k, cpr, static_cast<char*>(xp));
   return check_launch("moe_permute");
 }
 
@@ -189,7 +219,7 @@ extern "C" moe_status moe_unpermute(const void* yp, const int32_t* dest, const f
   if (moe_status s = check_move(T, k, d, dtype)) return s;
   MOE_REQUIRE(yp && dest && y, MOE_ERR_INVALID_ARG, "moe_unpermute: null pointer");
   const int cpr = static_cast<int>(d * dtype_size(dtype) / 16);
-  const dim3 grid(move_grid(static_cast<long long>(T) * cpr));
+  const dim3 grid(row_grid(T));
   if (dtype == MOE_BF16)
     hipLaunchKernelGGL(unpermute_kernel<uint16_t>, grid, dim3(kMoveBlock), 0, as_stream(stream),
                        static_cast<const char*>(yp), dest, w, T, k, cpr, static_cast<char*>(y));

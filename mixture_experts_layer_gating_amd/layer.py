@@ -13,7 +13,7 @@ method]):
     logits = x @ wr                    moe_grouped_gemm_fwd (one group, fp32 out)
     idx, w, p = top-k softmax          moe_route_topk
     counts, offsets, dest, src         moe_count_index
-    xp = x[src // k]                   moe_permute
+    xp[dest] = x (xp = x[src // k])    moe_permute
     h  = xp @ W1[e]                    moe_grouped_gemm_fwd
     a  = silu(h_gate) * h_up           moe_act_fwd
     yp = a @ W2[e]                     moe_grouped_gemm_fwd
@@ -125,7 +125,7 @@ class MoELayer:
             L.moe_count_index(self.idx, T, k, E, self.counts, self.offsets, self.dest, self.src,
                               self.ci_ws, self.ci_ws.numel(), stream=s)
         with self._span("permute"):
-            L.moe_permute(x, self.src, T, k, d, c, self.xp, stream=s)
+            L.moe_permute(x, self.dest, T, k, d, c, self.xp, stream=s)
         with self._span("gemm1_fwd"):
             L.moe_grouped_gemm_fwd(self.xp, w1, self.offsets, Tk, d, 2 * F, E, c, self.h, c,
                                    stream=s)

@@ -35,7 +35,7 @@ def _normal(shape, seed, scale=1.0, dtype="bf16"):
 
 # ------------------------------------------------------------------ permute / combine
 @pytest.mark.parametrize("T,k,E,d", [(1, 1, 1, 8), (37, 2, 5, 24), (1024, 8, 64, 2048),
-                                     (300, 3, 7, 136)])
+                                     (300, 3, 7, 136), (50, 10, 16, 64), (20, 32, 40, 32)])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_permute_unpermute(T, k, E, d, dtype):
     say(f"permute/unpermute T={T} k={k} E={E} d={d} {dtype}")
@@ -46,7 +46,7 @@ def test_permute_unpermute(T, k, E, d, dtype):
     x = _normal((T, d), 1, dtype=dtype)
     xd = dev(x, tdt)
     xp = torch.empty(T * k, d, dtype=tdt, device=DEV)
-    L.moe_permute(xd, dev(src), T, k, d, code, xp)
+    L.moe_permute(xd, dev(dest), T, k, d, code, xp)
     torch.cuda.synchronize()
     want = O.permute(x, src, k).astype(np.float32)
     if dtype == "bf16":
