@@ -175,9 +175,17 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
+// Buffer descriptor over [base, base + bytes).  Base and size are the same in
+// every lane; readfirstlane keeps the descriptor in scalar registers (a value
+// the compiler computes with vector instructions would otherwise make it wrap
+// every load in a loop over distinct descriptors).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long long bytes) {
   const int n = bytes > 0x7ffffff0LL ? 0x7ffffff0 : static_cast<int>(bytes < 0 ? 0 : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
+  void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, 0, __builtin_amdgcn_readfirstlane(n), 0x00020000);
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
@@ -219,14 +227,10 @@ struct DmaLoader {
   __amdgpu_buffer_rsrc_t rsrc;
   unsigned voff[kPerWave];  // byte offset at reduction step 0
   int lds_off[kPerWave];    // element offset in the stage tile (wave-uniform)
-  int cofs[kPerWave];       // k-contiguous: first reduction element of this lane's chunk
-  bool ok_o[kPerWave];
+  int klim[kPerWave];       // this lane's chunk is loaded for steps kt < klim
   unsigned step;            // bytes per reduction step of kBK
-  int r_hi, r_lo;
 
-  __device__ void init(const Operand& op, int r_lo_, int r_hi_) {
-    r_lo = r_lo_;
-    r_hi = r_hi_;
+  __device__ void init(const Operand& op, int r_lo, int r_hi) {
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;
 #pragma unroll
@@ -237,14 +241,16 @@ struct DmaLoader {
       if constexpr (!STRIDED) {
         const int row = pos / (kBK * 2);
         const int c = swz_c(row, lane & 3);  // logical chunk for physical chunk lane % 4
-        cofs[q] = c * 8;
-        ok_o[q] = row < op.o_valid;
+        // Chunk [c * 8, c * 8 + 8) of step kt lies inside the reduction range
+        // while r_lo + kt * kBK + c * 8 + 8 <= r_hi.
+        const int room = r_hi - r_lo - c * 8 - 8;
+        klim[q] = (row < op.o_valid && room >= 0) ? room / kBK + 1 : 0;
         voff[q] = static_cast<unsigned>((row * op.ld + c * 8) * 2);
       } else {
+        // Rows past the reduction range fall outside the buffer range.
         const int row = pos / (O * 2);
         const int u = ((pos % (O * 2)) / 16) ^ swz_t<O>(row);
-        cofs[q] = 0;
-        ok_o[q] = u * 8 + 8 <= op.o_valid;
+        klim[q] = (u * 8 + 8 <= op.o_valid) ? 0x7fffffff : 0;
         voff[q] = static_cast<unsigned>((row * op.ld + u * 8) * 2);
       }
     }
@@ -263,38 +269,64 @@ struct DmaLoader {
     if (kTotal < NW && static_cast<int>(threadIdx.x / kWave) >= kTotal) return;
 #pragma unroll
     for (int q = 0; q < kPerWave; ++q) {
-      bool ok = ok_o[q];
-      if constexpr (!STRIDED) ok = ok && (r_lo + kt * kBK + cofs[q] + 8 <= r_hi);
-      const unsigned off = ok ? voff[q] + static_cast<unsigned>(kt) * step : kOOB;
+      const unsigned off = kt < klim[q] ? voff[q] + static_cast<unsigned>(kt) * step : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(tile + lds_off[q]), 16, off,
                                                0, 0, 0);
     }
   }
 };
 
-// MFMA fragment: 8 consecutive k (16 kk .. 16 kk + 15 split by lane half) of
-// row / column `idx` of the tile.
-template <bool STRIDED, int O>
-__device__ __forceinline__ bf16x8 frag(const uint16_t* tile, int base, int kk, int lane) {
-  if constexpr (!STRIDED) {
-    const int row = base + (lane & 31);
-    const int chunk = kk * 2 + (lane >> 5);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(tile + row * kBK + (swz_c(row, chunk) << 3));
-    return __builtin_bit_cast(bf16x8, v);
-  } else {
-    const int g = lane >> 4, s = lane & 15;
-    const int col = base + 16 * (g & 1) + 4 * (s & 3);
-    const int k0 = 16 * kk + 8 * (g >> 1) + (s >> 2);
-    const int u = col >> 3, sub = col & 7;
-    const uint16_t* p0 = tile + k0 * O + ((u ^ swz_t<O>(k0)) << 3) + sub;
-    const uint16_t* p1 = tile + (k0 + 4) * O + ((u ^ swz_t<O>(k0 + 4)) << 3) + sub;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p0);
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p1);
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
-    const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8, v);
+// MFMA fragment addressing: 8 consecutive k (16 kk .. 16 kk + 15, split by
+// lane half) of row / column `32 i` of this wave's part of the stage tile.
+// The lane-dependent part of each LDS element offset is computed once per
+// tile; the rest is a compile-time constant that lands in the instruction's
+// offset field.  The lane part goes through an empty asm statement so that
+// every fragment read stays a plain offset from its stage array: the compiler
+// then keeps the LDS alias information that lets it wait only for the DMA
+// loads of the stage being read (when it derives one read's address from
+// another's, it drops that information and waits for all loads in flight).
+template <bool STRIDED, int O, int N>
+struct FragAddr {
+  int idx[STRIDED ? N : 2];
+
+  __device__ void init(int wbase, int lane) {
+    if constexpr (!STRIDED) {
+      // [O][32] tile, chunk c of row r at c ^ ((r >> 2) & 3); wbase % 32 == 0
+      const int row = wbase + (lane & 31);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int chunk = kk * 2 + (lane >> 5);
+        idx[kk] = row * kBK + (swz_c(row, chunk) << 3);
+        asm volatile("" : "+v"(idx[kk]));
+      }
+    } else {
+      // [32][O] tile; lane s of each 16 reads row k0 + s / 4, 4 columns from
+      // n0 + 4 (s % 4); the k0 + 4 and k0 + 16 rows share k0's swizzle.
+      const int g = lane >> 4, s = lane & 15;
+      const int k0 = 8 * (g >> 1) + (s >> 2);
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        const int col = wbase + j * 32 + 16 * (g & 1) + 4 * (s & 3);
+        idx[j] = k0 * O + (((col >> 3) ^ swz_t<O>(k0)) << 3) + (col & 7);
+        asm volatile("" : "+v"(idx[j]));
+      }
+    }
   }
-}
+
+  __device__ __forceinline__ bf16x8 read(const uint16_t* tile, int i, int kk) const {
+    if constexpr (!STRIDED) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(tile + idx[kk] + i * 32 * kBK);
+      return __builtin_bit_cast(bf16x8, v);
+    } else {
+      const uint16_t* p0 = tile + idx[i] + kk * 16 * O;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p0);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p0 + 4 * O));
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_bit_cast(bf16x8, v);
+    }
+  }
+};
 
 template <int MI, int NI>
 struct Frags {
@@ -303,14 +335,15 @@ struct Frags {
 
 // Fragments of the first MIV 32-row blocks of this wave's rows (the rest of
 // the wave's rows are past the end of its group) and all its columns.
-template <int MIV, bool XS, bool YS, int BM, int BN, int WM, int WN, int MI, int NI>
+template <int MIV, int MI, int NI, class XA, class YA>
 __device__ __forceinline__ void read_frags(Frags<MI, NI>& f, const uint16_t* xt,
-                                           const uint16_t* yt, int kk, int wm, int wn, int lane) {
+                                           const uint16_t* yt, int kk, const XA& xa,
+                                           const YA& ya) {
   if constexpr (MIV > 0) {
 #pragma unroll
-    for (int i = 0; i < MIV; ++i) f.a[i] = frag<XS, BM>(xt, wm * WM + i * 32, kk, lane);
+    for (int i = 0; i < MIV; ++i) f.a[i] = xa.read(xt, i, kk);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) f.b[j] = frag<YS, BN>(yt, wn * WN + j * 32, kk, lane);
+    for (int j = 0; j < NI; ++j) f.b[j] = ya.read(yt, j, kk);
   }
 }
 
@@ -326,11 +359,11 @@ __device__ __forceinline__ void mfma_step(f32x16 (&acc)[MI][NI], const Frags<MI,
 // The reduction loop of one workgroup tile.  Every wave issues its share of
 // the loads and takes part in every barrier; only the MFMAs (and fragment
 // reads) of row blocks past the end of the group are left out.
-template <int MIV, bool XS, bool YS, int BM, int BN, int WM, int WN, int MI, int NI, int LOADS,
-          class XL, class YL>
+template <int MIV, int BM, int BN, int MI, int NI, int LOADS, class XL, class YL, class XA,
+          class YA>
 __device__ __forceinline__ void reduce_tile(f32x16 (&acc)[MI][NI], const XL& xl, const YL& yl,
-                                            uint16_t* const (&stage)[kStages], int nk, int wm,
-                                            int wn, int lane) {
+                                            const XA& xa, const YA& ya,
+                                            uint16_t* const (&stage)[kStages], int nk) {
   constexpr int XE = BM * kBK;
   // Prologue: reduction steps 0..2 in flight, step 0 landed everywhere.
 #pragma unroll
@@ -341,7 +374,7 @@ __device__ __forceinline__ void reduce_tile(f32x16 (&acc)[MI][NI], const XL& xl,
   wait_vmcnt<2 * LOADS>();
   __builtin_amdgcn_s_barrier();
   Frags<MI, NI> f0, f1;
-  read_frags<MIV, XS, YS, BM, BN, WM, WN>(f0, stage[0], stage[0] + XE, 0, wm, wn, lane);
+  read_frags<MIV>(f0, stage[0], stage[0] + XE, 0, xa, ya);
   // Step kt (stage kt % 4):  MFMAs on k-slice 0 | read slice 1 | wait until
   // step kt+1 has landed, barrier | load step kt+3 into the stage step kt-1
   // used | MFMAs on slice 1 | read slice 0 of step kt+1.  Steps past the
@@ -353,13 +386,13 @@ __device__ __forceinline__ void reduce_tile(f32x16 (&acc)[MI][NI], const XL& xl,
       uint16_t* ld_stage = stage[(s + 3) & 3];
       const uint16_t* nxt = stage[(s + 1) & 3];
       mfma_step<MIV>(acc, f0);
-      read_frags<MIV, XS, YS, BM, BN, WM, WN>(f1, cur, cur + XE, 1, wm, wn, lane);
+      read_frags<MIV>(f1, cur, cur + XE, 1, xa, ya);
       wait_vmcnt<LOADS>();
       __builtin_amdgcn_s_barrier();
       xl.issue(ld_stage, kt + s + 3);
       yl.issue(ld_stage + XE, kt + s + 3);
       mfma_step<MIV>(acc, f1);
-      read_frags<MIV, XS, YS, BM, BN, WM, WN>(f0, nxt, nxt + XE, 0, wm, wn, lane);
+      read_frags<MIV>(f0, nxt, nxt + XE, 0, xa, ya);
     }
   }
   // Drain the loads of the last steps before the workgroup's LDS is released.
@@ -387,6 +420,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
 
   TileInfo t;
   if (!resolve_tile<MODE, BM>(p, sh, t)) return;
+  // The tile is the same for the whole workgroup; say so, so that buffer
+  // descriptors built from it live in scalar registers.
+  t.e = __builtin_amdgcn_readfirstlane(t.e);
+  t.i0 = __builtin_amdgcn_readfirstlane(t.i0);
+  t.j0 = __builtin_amdgcn_readfirstlane(t.j0);
+  t.r_lo = __builtin_amdgcn_readfirstlane(t.r_lo);
+  t.r_hi = __builtin_amdgcn_readfirstlane(t.r_hi);
+  t.g0 = __builtin_amdgcn_readfirstlane(t.g0);
+  t.g1 = __builtin_amdgcn_readfirstlane(t.g1);
   const int j0 = t.j0 * BN;
   const long long KN = static_cast<long long>(p.K) * p.N;
 
@@ -414,6 +456,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
   const int wm = wid / WGN, wn = wid % WGN;
+  FragAddr<XS, BM, MI> xa;
+  FragAddr<YS, BN, NI> ya;
+  xa.init(wm * WM, lane);
+  ya.init(wn * WN, lane);
 
   f32x16 acc[MI][NI];
 #pragma unroll
@@ -432,7 +478,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
     const int rem = rows - wm * WM;
     const int miv = rem <= 0 ? 0 : (rem >= WM ? MI : (rem + 31) / 32);
 #define MOE_REDUCE(V)                                                                     \
-  reduce_tile<V, XS, YS, BM, BN, WM, WN, MI, NI, LOADS>(acc, xl, yl, stage, nk, wm, wn, lane)
+  reduce_tile<V, BM, BN, MI, NI, LOADS>(acc, xl, yl, xa, ya, stage, nk)
     if (miv == MI) {
       MOE_REDUCE(MI);
     } else if constexpr (MI == 4) {
