@@ -191,8 +191,14 @@ moe_status moe_unpermute_bwd(const void* dy, const void* yp,
  *   da or db may be NULL to skip that product; da_add may be NULL.
  *
  * The bf16 path runs on MFMA tiles when K % 8 == 0 and N % 8 == 0; other
- * shapes and float32 run on a tiled FMA kernel.  ws/ws_bytes: reserved
- * workspace (moe_grouped_gemm_workspace_size() bytes; currently 0, NULL ok).
+ * shapes and float32 run on a tiled FMA kernel.  On the MFMA path every
+ * operand and result pointer must be 16-byte aligned (MOE_ERR_INVALID_ARG
+ * otherwise).  ws/ws_bytes: device workspace of at least
+ * moe_grouped_gemm_workspace_size() bytes, 16-byte aligned, used by
+ * moe_grouped_gemm_bwd for db when the weight gradient is reduced in row
+ * slices (shapes with few output tiles); MOE_ERR_WORKSPACE if it is needed
+ * and missing or too small.  The size is 0 (NULL allowed) when no slicing is
+ * planned; moe_grouped_gemm_fwd ignores it.
  */
 size_t moe_grouped_gemm_workspace_size(int M, int K, int N, int E,
                                        moe_dtype dtype);

@@ -147,28 +147,33 @@ __device__ bool resolve_tile(const GemmArgs& p, int* sh, TileInfo& t) {
 }
 
 // ------------------------------------------------------------------ MFMA path
-// Tiles of BM x BN outputs, reduction in steps of kBK = 32, kStages = 4 LDS
-// stages.  Operand tiles go from global memory straight into LDS
-// (buffer_load_dwordx4 ... lds: each wave instruction fills 1 KB of LDS, lane
-// i writing bytes [16 i, 16 i + 16)); the LDS layout is chosen through each
-// lane's source address.  Out-of-range elements come back as zeros from the
-// buffer descriptor's range check, so the main loop has no branches.
+// Tiles of BM x BN outputs, reduction in steps of kBK = 32.  Operand tiles go
+// from global memory straight into LDS (buffer_load_dwordx4 ... lds: each wave
+// instruction fills 1 KB of LDS, lane i writing bytes [16 i, 16 i + 16)); the
+// LDS layout is chosen through each lane's source address.  Out-of-range
+// elements come back as zeros from the buffer descriptor's range check, so the
+// main loop has no branches.
 //
-// LDS layouts (bf16):
-//   k-contiguous operand: [O][32], 64 B per row; 16-byte chunk c of row r is
-//     stored at chunk c ^ ((r >> 2) & 3).  MFMA fragments (8 consecutive k of
-//     one row) are read with ds_read_b128; 16 consecutive rows at one chunk
-//     cover all 64 banks.
-//   k-strided operand (the reduction index is not contiguous in memory): the
-//     tile is stored as it lies in memory, [32][O] (k rows of O contiguous
-//     elements); 16-byte unit u of row k is stored at u ^ swz_t(k).  Fragments
-//     are read with two ds_read_b64_tr_b16: within each 16 lanes, lane s
-//     reads 4 elements of row k0 + s/4 at column n0 + 4 (s % 4), and the
-//     instruction returns to lane s the 4 consecutive-k elements of column
-//     n0 + s -- the MFMA operand layout.
+// The load path is bound by the number of cache lines in flight per compute
+// unit, so every load fetches whole 128-byte lines:
+//   k-contiguous operand ("pair" buffers): two buffers of [O][64] (two
+//     reduction steps, 128 B per row), refilled every other step.  16-byte
+//     chunk c of row r is stored at chunk c ^ ((r >> 1) & 7); MFMA fragments
+//     (8 consecutive k of one row) are read with ds_read_b128, and 16
+//     consecutive rows at one chunk cover all 64 banks.
+//   k-strided operand ("quad" buffers; the reduction index is not contiguous
+//     in memory): four buffers of [32][O] (one step each, as the tile lies in
+//     memory, O >= 64 elements = whole lines).  16-byte unit u of row k is
+//     stored at u ^ swz_t(k).  Fragments are read with two ds_read_b64_tr_b16:
+//     within each 16 lanes, lane s reads 4 elements of row k0 + s/4 at column
+//     n0 + 4 (s % 4), and the instruction returns to lane s the 4
+//     consecutive-k elements of column n0 + s -- the MFMA operand layout.
+// Every wave waits for its own fragment reads of step s before the barrier
+// that ends step s, so the buffers of step s are free right after it: quad
+// loads for step s + 4 and (at odd s) pair loads for steps s + 3, s + 4 go out
+// then, three and two steps before they are read.
 constexpr int kBK = 32;
-constexpr int kStages = 4;
-constexpr int kThreads = 256;           // 4 waves, 2 x 2 over the tile
+constexpr int kThreads = 256;           // SIMT fallback: 256 threads per block
 constexpr unsigned kOOB = 0x80000000u;  // buffer offset that is always out of range
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -195,7 +200,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
-__device__ __forceinline__ int swz_c(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+// s_waitcnt vmcnt(N) lgkmcnt(0): this wave's LDS reads done and at most N of
+// its global loads outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);
+}
+
+// Pair buffers: physical 16-byte chunk of logical chunk c (0..7) of row r.
+__device__ __forceinline__ int swz_p(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
 template <int O>
 __device__ __forceinline__ int swz_t(int k) {
@@ -217,90 +231,105 @@ struct Operand {
   int o_valid;  // number of valid o from the tile's first one
 };
 
-// One operand of one stage: O x kBK elements = O / 16 KB, i.e. O / 16 wave
-// instructions shared by the NW waves of the workgroup.
+// Loads of one operand, shared by the NW waves of the workgroup.  A k-strided
+// operand loads one reduction step (O x 32 elements, O / 16 wave
+// instructions) per call; a k-contiguous one loads a pair of steps (O x 64
+// elements, O / 8 wave instructions).
 template <bool STRIDED, int O, int NW>
 struct DmaLoader {
-  static constexpr int kTotal = O / 16;
+  static constexpr int kSpan = STRIDED ? kBK : 2 * kBK;  // reduction elements per call
+  static constexpr int kTotal = O * kSpan * 2 / 1024;     // 1 KB wave instructions per call
   static constexpr int kPerWave = kTotal >= NW ? kTotal / NW : 1;
   static_assert(kTotal % NW == 0 || kTotal < NW, "chunks must split evenly over waves");
+  static_assert(NW % 2 == 0, "pair chunk mapping assumes an even number of waves");
   __amdgpu_buffer_rsrc_t rsrc;
-  unsigned voff[kPerWave];  // byte offset at reduction step 0
-  int lds_off[kPerWave];    // element offset in the stage tile (wave-uniform)
-  int klim[kPerWave];       // this lane's chunk is loaded for steps kt < klim
-  unsigned step;            // bytes per reduction step of kBK
+  unsigned voff[kPerWave];  // byte offset at call index 0 (kOOB: lane out of range)
+  int lds_off[kPerWave];    // element offset in the buffer (wave-uniform)
+  int klim;                 // k-contiguous: this lane's chunk loaded for call indices < klim
+  unsigned step;            // bytes per call index
 
-  __device__ void init(const Operand& op, int r_lo, int r_hi) {
+  __device__ __forceinline__ void init(const Operand& op, int r_lo, int r_hi) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int w = threadIdx.x / kWave;
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
 #pragma unroll
     for (int q = 0; q < kPerWave; ++q) {
-      const int cid = q * NW + w;  // 1 KB chunk of the stage tile
+      const int cid = q * NW + w;  // 1 KB piece of the buffer
       lds_off[q] = cid * 512;
-      const int pos = cid * 1024 + lane * 16;  // byte position in the tile
+      const int pos = cid * 1024 + lane * 16;  // byte position in the buffer
       if constexpr (!STRIDED) {
-        const int row = pos / (kBK * 2);
-        const int c = swz_c(row, lane & 3);  // logical chunk for physical chunk lane % 4
-        // Chunk [c * 8, c * 8 + 8) of step kt lies inside the reduction range
-        // while r_lo + kt * kBK + c * 8 + 8 <= r_hi.
+        // Row cid * 8 + lane / 8; its logical chunk c for physical chunk
+        // lane % 8 depends on the row only through (row / 2) % 8, i.e. on the
+        // lane and the parity of cid -- the same for every q (NW is even).
+        const int row = pos / (kSpan * 2);
+        const int c = swz_p(row, lane & 7);
+        // Chunk [c * 8, c * 8 + 8) of call i lies inside the reduction range
+        // while r_lo + i * 64 + c * 8 + 8 <= r_hi.
         const int room = r_hi - r_lo - c * 8 - 8;
-        klim[q] = (row < op.o_valid && room >= 0) ? room / kBK + 1 : 0;
-        voff[q] = static_cast<unsigned>((row * op.ld + c * 8) * 2);
+        klim = room >= 0 ? room / kSpan + 1 : 0;
+        voff[q] = row < op.o_valid ? static_cast<unsigned>((row * op.ld + c * 8) * 2) : kOOB;
       } else {
-        // Rows past the reduction range fall outside the buffer range.
+        // Rows past the reduction range fall outside the buffer range; so do
+        // columns past the operand (kOOB + i * step stays above the range,
+        // which is below 2^31 bytes).
         const int row = pos / (O * 2);
         const int u = ((pos % (O * 2)) / 16) ^ swz_t<O>(row);
-        klim[q] = (u * 8 + 8 <= op.o_valid) ? 0x7fffffff : 0;
-        voff[q] = static_cast<unsigned>((row * op.ld + u * 8) * 2);
+        voff[q] = (u * 8 + 8 <= op.o_valid) ? static_cast<unsigned>((row * op.ld + u * 8) * 2)
+                                            : kOOB;
       }
     }
     if constexpr (!STRIDED) {
       const int rows = op.o_valid < O ? (op.o_valid < 0 ? 0 : op.o_valid) : O;
       rsrc = make_rsrc(op.base, static_cast<long long>(rows) * op.ld * 2);
-      step = kBK * 2;
+      step = kSpan * 2;
     } else {
       rsrc = make_rsrc(op.base, static_cast<long long>(r_hi - r_lo) * op.ld * 2);
-      step = static_cast<unsigned>(kBK * op.ld * 2);
+      step = static_cast<unsigned>(kSpan * op.ld * 2);
     }
   }
 
-  // Issue the loads of reduction step kt into stage tile `tile`.
-  __device__ __forceinline__ void issue(uint16_t* tile, int kt) const {
+  // Issue the loads of call index i (a step, or a pair of steps) into `buf`.
+  __device__ __forceinline__ void issue(uint16_t* buf, int i) const {
     if (kTotal < NW && static_cast<int>(threadIdx.x / kWave) >= kTotal) return;
 #pragma unroll
     for (int q = 0; q < kPerWave; ++q) {
-      const unsigned off = kt < klim[q] ? voff[q] + static_cast<unsigned>(kt) * step : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(tile + lds_off[q]), 16, off,
-                                               0, 0, 0);
+      unsigned off;
+      if constexpr (STRIDED)
+        off = voff[q] + static_cast<unsigned>(i) * step;
+      else
+        off = i < klim ? voff[q] + static_cast<unsigned>(i) * step : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(buf + lds_off[q]), 16, off, 0,
+                                               0, 0);
     }
   }
 };
 
 // MFMA fragment addressing: 8 consecutive k (16 kk .. 16 kk + 15, split by
-// lane half) of row / column `32 i` of this wave's part of the stage tile.
-// The lane-dependent part of each LDS element offset is computed once per
-// tile; the rest is a compile-time constant that lands in the instruction's
-// offset field.  The lane part goes through an empty asm statement so that
-// every fragment read stays a plain offset from its stage array: the compiler
-// then keeps the LDS alias information that lets it wait only for the DMA
-// loads of the stage being read (when it derives one read's address from
-// another's, it drops that information and waits for all loads in flight).
+// lane half) of row / column `32 i` of this wave's part of the buffer, for the
+// step that is half h of a pair buffer (k-contiguous) or a whole quad buffer
+// (k-strided).  The lane-dependent part of each LDS element offset is
+// computed once per tile; the rest is a compile-time constant that lands in
+// the instruction's offset field.  The lane part goes through an empty asm
+// statement so that every fragment read stays a plain offset from its buffer
+// array: the compiler then keeps the LDS alias information that lets it wait
+// only for the DMA loads of the buffer being read (when it derives one read's
+// address from another's, it drops that information and waits for all loads
+// in flight).
 template <bool STRIDED, int O, int N>
 struct FragAddr {
-  int idx[STRIDED ? N : 2];
+  int idx[STRIDED ? N : 4];
 
-  __device__ void init(int wbase, int lane) {
+  __device__ __forceinline__ void init(int wbase, int lane) {
     if constexpr (!STRIDED) {
-      // [O][32] tile, chunk c of row r at c ^ ((r >> 2) & 3); wbase % 32 == 0
+      // [O][64] buffer; wbase % 32 == 0, so the swizzle depends on the lane only
       const int row = wbase + (lane & 31);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int chunk = kk * 2 + (lane >> 5);
-        idx[kk] = row * kBK + (swz_c(row, chunk) << 3);
-        asm volatile("" : "+v"(idx[kk]));
+      for (int hk = 0; hk < 4; ++hk) {
+        const int chunk = hk * 2 + (lane >> 5);  // hk = 2 h + kk
+        idx[hk] = row * 2 * kBK + (swz_p(row, chunk) << 3);
+        asm volatile("" : "+v"(idx[hk]));
       }
     } else {
-      // [32][O] tile; lane s of each 16 reads row k0 + s / 4, 4 columns from
+      // [32][O] buffer; lane s of each 16 reads row k0 + s / 4, 4 columns from
       // n0 + 4 (s % 4); the k0 + 4 and k0 + 16 rows share k0's swizzle.
       const int g = lane >> 4, s = lane & 15;
       const int k0 = 8 * (g >> 1) + (s >> 2);
@@ -313,12 +342,13 @@ struct FragAddr {
     }
   }
 
-  __device__ __forceinline__ bf16x8 read(const uint16_t* tile, int i, int kk) const {
+  __device__ __forceinline__ bf16x8 read(const uint16_t* buf, int i, int h, int kk) const {
     if constexpr (!STRIDED) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(tile + idx[kk] + i * 32 * kBK);
+      const u32x4 v =
+          *reinterpret_cast<const u32x4*>(buf + idx[h * 2 + kk] + i * 32 * 2 * kBK);
       return __builtin_bit_cast(bf16x8, v);
     } else {
-      const uint16_t* p0 = tile + idx[i] + kk * 16 * O;
+      const uint16_t* p0 = buf + idx[i] + kk * 16 * O;
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p0);
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p0 + 4 * O));
       typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -333,17 +363,30 @@ struct Frags {
   bf16x8 a[MI], b[NI];
 };
 
-// Fragments of the first MIV 32-row blocks of this wave's rows (the rest of
-// the wave's rows are past the end of its group) and all its columns.
-template <int MIV, int MI, int NI, class XA, class YA>
-__device__ __forceinline__ void read_frags(Frags<MI, NI>& f, const uint16_t* xt,
-                                           const uint16_t* yt, int kk, const XA& xa,
-                                           const YA& ya) {
+// Buffers of one operand: four quad buffers or two pair buffers.
+struct Bufs {
+  uint16_t* b[4];
+};
+
+// Buffer and pair half holding reduction step s (mod 4) of an operand.
+template <bool STRIDED>
+__device__ __forceinline__ const uint16_t* step_buf(const Bufs& B, int s) {
+  return STRIDED ? B.b[s & 3] : B.b[(s >> 1) & 1];
+}
+
+// Fragments of step s (mod 4), k-slice kk: the first MIV 32-row blocks of this
+// wave's rows (the rest of the wave's rows are past the end of its group) and
+// all its columns.
+template <int MIV, bool XS, bool YS, int MI, int NI, class XA, class YA>
+__device__ __forceinline__ void read_frags(Frags<MI, NI>& f, const Bufs& xb, const Bufs& yb,
+                                           int s, int kk, const XA& xa, const YA& ya) {
   if constexpr (MIV > 0) {
+    const uint16_t* xt = step_buf<XS>(xb, s);
+    const uint16_t* yt = step_buf<YS>(yb, s);
 #pragma unroll
-    for (int i = 0; i < MIV; ++i) f.a[i] = xa.read(xt, i, kk);
+    for (int i = 0; i < MIV; ++i) f.a[i] = xa.read(xt, i, s & 1, kk);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) f.b[j] = ya.read(yt, j, kk);
+    for (int j = 0; j < NI; ++j) f.b[j] = ya.read(yt, j, s & 1, kk);
   }
 }
 
@@ -356,43 +399,63 @@ __device__ __forceinline__ void mfma_step(f32x16 (&acc)[MI][NI], const Frags<MI,
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
+// Loads that belong to reduction step t (t % 4 == s, a compile-time
+// constant): quad operands load step t into quad buffer s; when t is odd, pair
+// operands load steps t - 1, t (pair (t - 1) / 2) into pair buffer
+// ((t - 1) / 2) % 2 -- two steps ahead of the quad loads of step t - 1, since a
+// pair buffer frees up only after both steps of the pair it held.
+template <bool XS, bool YS, class XL, class YL>
+__device__ __forceinline__ void issue_step(const XL& xl, const YL& yl, const Bufs& xb,
+                                           const Bufs& yb, int s, int t) {
+  if ((s & 1) == 1) {
+    if constexpr (!XS) xl.issue(xb.b[(s >> 1) & 1], t >> 1);
+    if constexpr (!YS) yl.issue(yb.b[(s >> 1) & 1], t >> 1);
+  }
+  if constexpr (XS) xl.issue(xb.b[s & 3], t);
+  if constexpr (YS) yl.issue(yb.b[s & 3], t);
+}
+
 // The reduction loop of one workgroup tile.  Every wave issues its share of
 // the loads and takes part in every barrier; only the MFMAs (and fragment
 // reads) of row blocks past the end of the group are left out.
-template <int MIV, int BM, int BN, int MI, int NI, int LOADS, class XL, class YL, class XA,
-          class YA>
+//
+// Step s:  read k-slice 1 of step s | MFMAs on slice 0 | wait for this wave's
+// reads and for the loads step s + 1 needs, barrier | issue the loads of step
+// s + 4 | MFMAs on slice 1 | read slice 0 of step s + 1.  Loads go out in
+// step order (a step's pair before its quads), so what step s + 1 needs --
+// its quads, issued with step s + 1, and when s + 1 is even its pair, issued
+// with step s + 2 -- has landed once no more than the loads of the later
+// steps up to s + 3 are outstanding.  Steps past the reduction range load
+// zeros; the loop runs a multiple of 4 steps.
+template <int MIV, bool XS, bool YS, int MI, int NI, class XL, class YL, class XA, class YA>
 __device__ __forceinline__ void reduce_tile(f32x16 (&acc)[MI][NI], const XL& xl, const YL& yl,
-                                            const XA& xa, const YA& ya,
-                                            uint16_t* const (&stage)[kStages], int nk) {
-  constexpr int XE = BM * kBK;
-  // Prologue: reduction steps 0..2 in flight, step 0 landed everywhere.
+                                            const XA& xa, const YA& ya, const Bufs& xb,
+                                            const Bufs& yb, int nk) {
+  constexpr int LQ = (XS ? XL::kPerWave : 0) + (YS ? YL::kPerWave : 0);  // per quad step
+  constexpr int LP = (XS ? 0 : XL::kPerWave) + (YS ? 0 : YL::kPerWave);  // per pair
+  // Prologue: steps 0..3 in flight (pairs 0 and 1 with steps 1 and 3), step
+  // 0 landed everywhere.
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) {
-    xl.issue(stage[s], s);
-    yl.issue(stage[s] + XE, s);
-  }
-  wait_vmcnt<2 * LOADS>();
+  for (int s = 0; s < 4; ++s) issue_step<XS, YS>(xl, yl, xb, yb, s, s);
+  wait_vmcnt<3 * LQ + LP>();
   __builtin_amdgcn_s_barrier();
   Frags<MI, NI> f0, f1;
-  read_frags<MIV>(f0, stage[0], stage[0] + XE, 0, xa, ya);
-  // Step kt (stage kt % 4):  MFMAs on k-slice 0 | read slice 1 | wait until
-  // step kt+1 has landed, barrier | load step kt+3 into the stage step kt-1
-  // used | MFMAs on slice 1 | read slice 0 of step kt+1.  Steps past the
-  // reduction range load zeros; the loop runs a multiple of 4 steps.
-  for (int kt = 0; kt < nk; kt += kStages) {
+  read_frags<MIV, XS, YS>(f0, xb, yb, 0, 0, xa, ya);
+  for (int kt = 0; kt < nk; kt += 4) {
 #pragma unroll
-    for (int s = 0; s < kStages; ++s) {
-      const uint16_t* cur = stage[s];
-      uint16_t* ld_stage = stage[(s + 3) & 3];
-      const uint16_t* nxt = stage[(s + 1) & 3];
+    for (int s = 0; s < 4; ++s) {
+      read_frags<MIV, XS, YS>(f1, xb, yb, s, 1, xa, ya);
       mfma_step<MIV>(acc, f0);
-      read_frags<MIV>(f1, cur, cur + XE, 1, xa, ya);
-      wait_vmcnt<LOADS>();
+      // Issued after the loads step s + 1 needs: steps s + 2 and s + 3, minus
+      // the pair of step s + 2 when that is the pair step s + 1 needs.
+      if ((s & 1) == 0)
+        wait_vmcnt_lgkm0<2 * LQ + LP>();
+      else
+        wait_vmcnt_lgkm0<2 * LQ>();
       __builtin_amdgcn_s_barrier();
-      xl.issue(ld_stage, kt + s + 3);
-      yl.issue(ld_stage + XE, kt + s + 3);
+      issue_step<XS, YS>(xl, yl, xb, yb, s, kt + s + 4);
       mfma_step<MIV>(acc, f1);
-      read_frags<MIV>(f0, nxt, nxt + XE, 0, xa, ya);
+      read_frags<MIV, XS, YS>(f0, xb, yb, s + 1, 0, xa, ya);
     }
   }
   // Drain the loads of the last steps before the workgroup's LDS is released.
@@ -407,15 +470,19 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int MI = WM / 32, NI = WN / 32;
-  constexpr int XE = BM * kBK, YE = BN * kBK;  // elements per stage tile
-  // DMA instructions per thread per stage
-  constexpr int LOADS = DmaLoader<XS, BM, NW>::kPerWave + DmaLoader<YS, BN, NW>::kPerWave;
-  // One array per stage: the compiler then tracks each stage's loads
+  // Elements per buffer: four quad buffers (k-strided) or two pair buffers.
+  constexpr int XBE = XS ? BM * kBK : BM * 2 * kBK;
+  constexpr int YBE = YS ? BN * kBK : BN * 2 * kBK;
+  // One array per buffer: the compiler then tracks each buffer's loads
   // separately and waits only for the ones a read depends on.
-  __shared__ __attribute__((aligned(1024))) uint16_t st0[XE + YE];
-  __shared__ __attribute__((aligned(1024))) uint16_t st1[XE + YE];
-  __shared__ __attribute__((aligned(1024))) uint16_t st2[XE + YE];
-  __shared__ __attribute__((aligned(1024))) uint16_t st3[XE + YE];
+  __shared__ __attribute__((aligned(1024))) uint16_t xb0[XBE];
+  __shared__ __attribute__((aligned(1024))) uint16_t xb1[XBE];
+  __shared__ alignas(XS ? 1024 : 16) uint16_t xb2[XS ? XBE : 8];
+  __shared__ alignas(XS ? 1024 : 16) uint16_t xb3[XS ? XBE : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t yb0[YBE];
+  __shared__ __attribute__((aligned(1024))) uint16_t yb1[YBE];
+  __shared__ alignas(YS ? 1024 : 16) uint16_t yb2[YS ? YBE : 8];
+  __shared__ alignas(YS ? 1024 : 16) uint16_t yb3[YS ? YBE : 8];
   __shared__ int sh[4];
 
   TileInfo t;
@@ -471,14 +538,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
 
   const int nk = (t.r_hi - t.r_lo + kBK - 1) / kBK;
   if (nk > 0) {
-    uint16_t* const stage[kStages] = {st0, st1, st2, st3};
+    const Bufs xb = {{xb0, xb1, xb2, xb3}};
+    const Bufs yb = {{yb0, yb1, yb2, yb3}};
     // Row blocks of this wave that hold rows of the tile (partial last tiles
     // of a group, or of K in the weight-gradient layout).
     const int rows = (MODE == kTN) ? p.K - t.i0 : t.g1 - t.i0;
     const int rem = rows - wm * WM;
     const int miv = rem <= 0 ? 0 : (rem >= WM ? MI : (rem + 31) / 32);
-#define MOE_REDUCE(V)                                                                     \
-  reduce_tile<V, BM, BN, MI, NI, LOADS>(acc, xl, yl, xa, ya, stage, nk)
+#define MOE_REDUCE(V) reduce_tile<V, XS, YS, MI, NI>(acc, xl, yl, xa, ya, xb, yb, nk)
     if (miv == MI) {
       MOE_REDUCE(MI);
     } else if constexpr (MI == 4) {
@@ -496,7 +563,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
   }
 
   // Epilogue.  32x32 accumulator layout: lane l, register r holds
-  // row (r/4)*8 + (l/32)*4 + r%4, column l%32.
+  // row (r/4)*8 + (l/32)*4 + r%4, column l%32.  Consecutive lanes write
+  // consecutive columns, so each store instruction covers two 64-byte row
+  // segments (bf16).  (Whole-tile stores leave every compute unit at once;
+  // wider per-lane stores only make that burst denser.)
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -704,7 +774,18 @@ Waves waves_of(Cfg c) {
   return {2, 2};
 }
 
-bool mfma_ok(moe_dtype dt, int K, int N) { return dt == MOE_BF16 && K % 8 == 0 && N % 8 == 0; }
+// The MFMA kernels address operands through buffer descriptors with 32-bit
+// byte offsets: every operand (and one expert's weights) stays below 2^31
+// bytes.  Larger shapes take the FMA kernel.
+bool mfma_ok(moe_dtype dt, int M, int K, int N) {
+  const long long lim = 1ll << 30;  // elements of 2 bytes
+  return dt == MOE_BF16 && K % 8 == 0 && N % 8 == 0 && static_cast<long long>(M) * K < lim &&
+         static_cast<long long>(M) * N < lim && static_cast<long long>(K) * N < lim;
+}
+
+// The MFMA kernels move 16-byte vectors: operands and results start on
+// 16-byte boundaries (null pointers pass).
+bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; }
 
 template <int MODE, int BM, int BN, int WGM, int WGN, typename OutT>
 void launch_mfma(GemmArgs p, long long tiles_upper, hipStream_t st) {
@@ -765,7 +846,7 @@ moe_status check_gemm(const void* offsets, int M, int K, int N, int E, moe_dtype
 using namespace moe;
 
 extern "C" size_t moe_grouped_gemm_workspace_size(int M, int K, int N, int E, moe_dtype dtype) {
-  if (M < 1 || K < 1 || N < 1 || E < 1 || !mfma_ok(dtype, K, N)) return 0;
+  if (M < 1 || K < 1 || N < 1 || E < 1 || !mfma_ok(dtype, M, K, N)) return 0;
   const int s = pick_split(M, K, N, E);
   if (s <= 1) return 0;
   return static_cast<size_t>(s) * E * K * N * sizeof(float);
@@ -780,7 +861,7 @@ extern "C" moe_status moe_grouped_gemm_plan(int product, int M, int K, int N, in
   MOE_REQUIRE(M >= 1 && K >= 1 && N >= 1 && E >= 1, MOE_ERR_INVALID_ARG,
               "moe_grouped_gemm_plan: sizes must be >= 1");
   MOE_REQUIRE(dtype_ok(dtype), MOE_ERR_UNSUPPORTED, "moe_grouped_gemm_plan: unknown dtype");
-  const bool m = mfma_ok(dtype, K, N);
+  const bool m = mfma_ok(dtype, M, K, N);
   Cfg c{kSimtTile, kSimtTile};
   int s = 1;
   if (m) {
@@ -818,9 +899,12 @@ extern "C" moe_status moe_grouped_gemm_fwd(const void* a, const void* b, const i
   MOE_REQUIRE(dtype_ok(c_dtype), MOE_ERR_UNSUPPORTED, "moe_grouped_gemm_fwd: bad c_dtype");
   MOE_REQUIRE(!(ab_dtype == MOE_F32 && c_dtype == MOE_BF16), MOE_ERR_UNSUPPORTED,
               "moe_grouped_gemm_fwd: float32 inputs need a float32 output");
+  if (mfma_ok(ab_dtype, M, K, N))
+    MOE_REQUIRE(aligned16(a) && aligned16(b) && aligned16(c), MOE_ERR_INVALID_ARG,
+                "moe_grouped_gemm_fwd: bf16 operands and result must be 16-byte aligned");
   GemmArgs p{a, b, nullptr, c, offsets, M, K, N, E, 0, 0, 1};
   hipStream_t st = as_stream(stream);
-  if (mfma_ok(ab_dtype, K, N)) {
+  if (mfma_ok(ab_dtype, M, K, N)) {
     const Cfg cfg = pick_row_cfg(M, E, N);
     if (c_dtype == MOE_BF16) dispatch_mfma<kNN, uint16_t>(cfg, p, st);
     else dispatch_mfma<kNN, float>(cfg, p, st);
@@ -845,7 +929,12 @@ extern "C" moe_status moe_grouped_gemm_bwd(const void* a, const void* b, const v
               "moe_grouped_gemm_bwd: da needs b");
   MOE_REQUIRE(db == nullptr || a != nullptr, MOE_ERR_INVALID_ARG,
               "moe_grouped_gemm_bwd: db needs a");
-  const bool use_mfma = mfma_ok(dtype, K, N);
+  const bool use_mfma = mfma_ok(dtype, M, K, N);
+  if (use_mfma)
+    MOE_REQUIRE(aligned16(a) && aligned16(b) && aligned16(dc) && aligned16(da) &&
+                    aligned16(da_add) && aligned16(db),
+                MOE_ERR_INVALID_ARG,
+                "moe_grouped_gemm_bwd: bf16 operands and results must be 16-byte aligned");
   int split = 1;
   if (db && use_mfma) {
     split = pick_split(M, K, N, E);

@@ -83,3 +83,9 @@ def test_gemm_validation_and_workspace():
     assert _rc("moe_grouped_gemm_fwd", FAKE, FAKE, FAKE, 0, 8, 8, 1, L.MOE_BF16, FAKE, L.MOE_BF16, None, 0, None) == L.MOE_ERR_INVALID_ARG
     assert _rc("moe_grouped_gemm_bwd", FAKE, FAKE, FAKE, FAKE, 8192, 2048, 64, 1, L.MOE_BF16, None, None, FAKE, None, 0, None) == L.MOE_ERR_WORKSPACE
     assert _rc("moe_grouped_gemm_bwd", FAKE, None, FAKE, FAKE, 16, 8, 8, 1, L.MOE_BF16, FAKE, None, None, None, 0, None) == L.MOE_ERR_INVALID_ARG
+    # the MFMA path moves 16-byte vectors: misaligned operands are rejected
+    odd = FAKE + 8
+    assert _rc("moe_grouped_gemm_fwd", odd, FAKE, FAKE, 4, 8, 8, 1, L.MOE_BF16, FAKE, L.MOE_BF16, None, 0, None) == L.MOE_ERR_INVALID_ARG
+    assert _rc("moe_grouped_gemm_fwd", FAKE, FAKE, FAKE, 4, 8, 8, 1, L.MOE_BF16, odd, L.MOE_F32, None, 0, None) == L.MOE_ERR_INVALID_ARG
+    assert _rc("moe_grouped_gemm_bwd", FAKE, FAKE, FAKE, FAKE, 16, 8, 8, 1, L.MOE_BF16, odd, None, None, None, 0, None) == L.MOE_ERR_INVALID_ARG
+    assert _rc("moe_grouped_gemm_bwd", FAKE, FAKE, FAKE, FAKE, 16, 8, 8, 1, L.MOE_BF16, FAKE, odd, None, None, 0, None) == L.MOE_ERR_INVALID_ARG
