@@ -52,42 +52,88 @@ struct GemmArgs {
 // Row-tiled modes (NN, NT): wave 0 finds which expert owns this workgroup's
 // row tile.  Tiles are counted per expert as ceil(rows_e / BM); logical tile
 // L = row_tile * ntn + col_tile; workgroup b runs on XCD b % 8 and takes
-// logical tile (b % 8) * ceil(n / 8) + b / 8.
+// logical tile (b % 8) * ceil(n / 8) + b / 8.  Up to kHeld * 64 experts the
+// offsets are loaded once (all loads in flight together) and kept in
+// registers; the expert's row range goes back through sh[] so that no thread
+// reloads it.
 template <int BM>
 __device__ void find_row_tile(const int32_t* __restrict__ offsets, int E, int ntn, int lane,
                               int* sh) {
+  constexpr int kHeld = 4;
+  const bool held = E <= kHeld * kWave;
+  int o0[kHeld], o1[kHeld], tiles[kHeld], incl[kHeld];
   int total = 0;
-  for (int c = 0; c < E; c += kWave) {
-    const int e = c + lane;
-    int tiles = 0;
-    if (e < E) tiles = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
-    total += wave_sum_int(tiles);
+  if (held) {
+#pragma unroll
+    for (int c = 0; c < kHeld; ++c) {
+      const int e = c * kWave + lane;
+      o0[c] = e < E ? offsets[e] : 0;
+      o1[c] = e < E ? offsets[e + 1] : 0;
+    }
+#pragma unroll
+    for (int c = 0; c < kHeld; ++c) {
+      tiles[c] = (o1[c] - o0[c] + BM - 1) / BM;
+      incl[c] = 0;
+      if (c * kWave < E) {
+        incl[c] = wave_inclusive_scan(tiles[c], lane);
+        total += __shfl(incl[c], kWave - 1, kWave);
+      }
+    }
+  } else {
+    for (int c = 0; c < E; c += kWave) {
+      const int e = c + lane;
+      int n = 0;
+      if (e < E) n = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+      total += wave_sum_int(n);
+    }
   }
   const long long n_act = static_cast<long long>(total) * ntn;
   const long long per = (n_act + 7) / 8;
   const long long rank = blockIdx.x >> 3;
   const long long L = static_cast<long long>(blockIdx.x & 7) * per + rank;
-  int found = 0, e_found = 0, mt_local = 0, nt = 0;
+  int found = 0, e_found = 0, mt_local = 0, nt = 0, g0 = 0, g1 = 0;
   if (rank < per && L < n_act) {
     const int mt = static_cast<int>(L / ntn);
     nt = static_cast<int>(L - static_cast<long long>(mt) * ntn);
     int carry = 0;
-    for (int c = 0; c < E; c += kWave) {
-      const int e = c + lane;
-      int tiles = 0;
-      if (e < E) tiles = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
-      const int inc = wave_inclusive_scan(tiles, lane);
-      const int excl = carry + inc - tiles;
-      const bool hit = tiles > 0 && mt >= excl && mt < excl + tiles;
-      const uint64_t bal = __ballot(hit);
-      if (bal) {
-        const int srcl = __builtin_ctzll(bal);
-        e_found = __shfl(e, srcl, kWave);
-        mt_local = mt - __shfl(excl, srcl, kWave);
-        found = 1;
-        break;
+    if (held) {
+#pragma unroll
+      for (int c = 0; c < kHeld; ++c) {
+        if (found || c * kWave >= E) continue;
+        const int excl = carry + incl[c] - tiles[c];
+        const bool hit = tiles[c] > 0 && mt >= excl && mt < excl + tiles[c];
+        const uint64_t bal = __ballot(hit);
+        if (bal) {
+          const int srcl = __builtin_ctzll(bal);
+          e_found = c * kWave + srcl;
+          mt_local = mt - __shfl(excl, srcl, kWave);
+          g0 = __shfl(o0[c], srcl, kWave);
+          g1 = __shfl(o1[c], srcl, kWave);
+          found = 1;
+        }
+        carry += __shfl(incl[c], kWave - 1, kWave);
       }
-      carry += __shfl(inc, kWave - 1, kWave);
+    } else {
+      for (int c = 0; c < E; c += kWave) {
+        const int e = c + lane;
+        const int a0 = e < E ? offsets[e] : 0;
+        const int a1 = e < E ? offsets[e + 1] : 0;
+        const int n = (a1 - a0 + BM - 1) / BM;
+        const int inc = wave_inclusive_scan(n, lane);
+        const int excl = carry + inc - n;
+        const bool hit = n > 0 && mt >= excl && mt < excl + n;
+        const uint64_t bal = __ballot(hit);
+        if (bal) {
+          const int srcl = __builtin_ctzll(bal);
+          e_found = __shfl(e, srcl, kWave);
+          mt_local = mt - __shfl(excl, srcl, kWave);
+          g0 = __shfl(a0, srcl, kWave);
+          g1 = __shfl(a1, srcl, kWave);
+          found = 1;
+          break;
+        }
+        carry += __shfl(inc, kWave - 1, kWave);
+      }
     }
   }
   if (lane == 0) {
@@ -95,6 +141,8 @@ __device__ void find_row_tile(const int32_t* __restrict__ offsets, int E, int nt
     sh[1] = e_found;
     sh[2] = mt_local;
     sh[3] = nt;
+    sh[4] = g0;
+    sh[5] = g1;
   }
 }
 
@@ -135,8 +183,8 @@ __device__ bool resolve_tile(const GemmArgs& p, int* sh, TileInfo& t) {
     __syncthreads();
     if (!sh[0]) return false;
     t.e = sh[1];
-    t.g0 = p.offsets[t.e];
-    t.g1 = p.offsets[t.e + 1];
+    t.g0 = sh[4];
+    t.g1 = sh[5];
     t.i0 = t.g0 + sh[2] * BM;
     t.j0 = sh[3];
     t.r_lo = 0;
@@ -483,7 +531,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
   __shared__ __attribute__((aligned(1024))) uint16_t yb1[YBE];
   __shared__ alignas(YS ? 1024 : 16) uint16_t yb2[YS ? YBE : 8];
   __shared__ alignas(YS ? 1024 : 16) uint16_t yb3[YS ? YBE : 8];
-  __shared__ int sh[4];
+  __shared__ int sh[8];
 
   TileInfo t;
   if (!resolve_tile<MODE, BM>(p, sh, t)) return;
@@ -624,7 +672,7 @@ template <int MODE, typename InT, typename OutT>
 __global__ __launch_bounds__(kThreads) void gemm_simt_kernel(GemmArgs p) {
   __shared__ float xs[kSimtBK][kSimtTile + 4];
   __shared__ float ys[kSimtBK][kSimtTile + 4];
-  __shared__ int sh[4];
+  __shared__ int sh[8];
   TileInfo t;
   if (!resolve_tile<MODE, kSimtTile>(p, sh, t)) return;
   const int j0 = t.j0 * kSimtTile;

@@ -128,6 +128,7 @@ GEMM_CASES = [
     (4096, 200, 264, 3, "skew"),         # K, N not multiples of 64
     (777, 64, 128, 4, "one"),            # every row in the last group
     (333, 12, 20, 3, "random"),          # K, N not multiples of 8 -> FMA kernel
+    (2400, 64, 128, 300, "random"),      # more groups than the tile scan keeps in registers
 ]
 
 
