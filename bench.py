@@ -54,6 +54,7 @@ def call_work(wl, b):
     f["permute"] = (0, T * d * b + Tk * d * b + Tk * 4)
     f["gemm1_fwd"] = (2 * Tk * d * 2 * F, Tk * d * b + E * d * 2 * F * b + Tk * 2 * F * b)
     f["act_fwd"] = (0, Tk * 2 * F * b + Tk * F * b)
+    f["gemm1_swiglu_fwd"] = (f["gemm1_fwd"][0], f["gemm1_fwd"][1] + Tk * F * b)
     f["gemm2_fwd"] = (2 * Tk * F * d, Tk * F * b + E * F * d * b + Tk * d * b)
     f["unpermute"] = (0, Tk * d * b + T * d * b + Tk * 8)
     f["unpermute_bwd"] = (0, T * d * b + 2 * Tk * d * b + Tk * 12)
@@ -72,6 +73,7 @@ def call_work(wl, b):
 GEMM_CALLS = {  # call -> (product, M, K, N, E) builder
     "router_fwd": lambda wl: (0, wl.T, wl.d, wl.E, 1),
     "gemm1_fwd": lambda wl: (0, wl.T * wl.k, wl.d, 2 * wl.F, wl.E),
+    "gemm1_swiglu_fwd": lambda wl: (3, wl.T * wl.k, wl.d, 2 * wl.F, wl.E),
     "gemm2_fwd": lambda wl: (0, wl.T * wl.k, wl.F, wl.d, wl.E),
     "gemm2_bwd_da": lambda wl: (1, wl.T * wl.k, wl.F, wl.d, wl.E),
     "gemm2_bwd_dw": lambda wl: (2, wl.T * wl.k, wl.F, wl.d, wl.E),
@@ -80,8 +82,8 @@ GEMM_CALLS = {  # call -> (product, M, K, N, E) builder
     "router_bwd_da": lambda wl: (1, wl.T, wl.d, wl.E, 1),
     "router_bwd_dw": lambda wl: (2, wl.T, wl.d, wl.E, 1),
 }
-EXPERT_GEMMS = ("gemm1_fwd", "gemm2_fwd", "gemm2_bwd_da", "gemm2_bwd_dw", "gemm1_bwd_da",
-                "gemm1_bwd_dw")
+EXPERT_GEMMS = ("gemm1_swiglu_fwd", "gemm2_fwd", "gemm2_bwd_da", "gemm2_bwd_dw",
+                "gemm1_bwd_da", "gemm1_bwd_dw")
 
 
 def kernel_name(L, call, wl, code):
@@ -90,9 +92,11 @@ def kernel_name(L, call, wl, code):
     plan = L.moe_grouped_gemm_plan(prod, M, K, N, E, code)
     if not plan["mfma"]:
         return f"gemm_simt_kernel<{prod}, ...>"
-    out = "unsigned short" if prod == 1 or (prod == 0 and call != "router_fwd") else "float"
-    return (f"gemm_mfma_kernel<{prod}, {plan['tile_m']}, {plan['tile_n']}, "
-            f"{plan['waves_m']}, {plan['waves_n']}, {out}>")
+    out = "float" if prod == 2 or call == "router_fwd" else "unsigned short"
+    mode = 0 if prod == 3 else prod
+    glu = "true" if prod == 3 else "false"
+    return (f"gemm_mfma_kernel<{mode}, {plan['tile_m']}, {plan['tile_n']}, "
+            f"{plan['waves_m']}, {plan['waves_n']}, {out}, {glu}>")
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -358,6 +362,8 @@ def main():
     # Dominant kernel: the GEMM kernel instance with the largest time per step.
     by_kernel = {}
     for n in GEMM_CALLS:
+        if n not in kernels:  # (gemm1_fwd runs fused with the activation)
+            continue
         kname = kernels[n]["kernel"]
         agg = by_kernel.setdefault(kname, {"ms": 0.0, "flops": 0, "launches": 0})
         agg["ms"] += kernels[n]["ms"]

@@ -206,7 +206,7 @@ size_t moe_grouped_gemm_workspace_size(int M, int K, int N, int E,
  * moe_grouped_gemm_plan -- the kernel configuration the grouped GEMM entry
  * points choose for a shape (host-only query, enqueues nothing).
  * product: 0 = forward c (moe_grouped_gemm_fwd), 1 = da, 2 = db
- * (moe_grouped_gemm_bwd).  Writes the row/column tile sizes, the wavefront
+ * (moe_grouped_gemm_bwd), 3 = h of moe_grouped_gemm_swiglu_fwd (N = 2F).  Writes the row/column tile sizes, the wavefront
  * grid of a workgroup (waves_m x waves_n), and the number of reduction
  * slices; *mfma = 1 for the bf16 MFMA kernel, 0 for the FMA kernel.  Any
  * output pointer may be NULL.
@@ -225,6 +225,27 @@ moe_status moe_grouped_gemm_bwd(const void* a, const void* b, const void* dc,
                                 int E, moe_dtype dtype, void* da,
                                 const void* da_add, float* db, void* ws,
                                 size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * moe_grouped_gemm_swiglu_fwd -- GEMM 1 with the SwiGLU activation in its
+ * epilogue [Summary, Method details / key design: optimised matrix
+ * multiplication and activation function].  For the rows of every group e:
+ *   h[rows e]  = a[rows e] @ b[e]                 [M, 2F], dtype
+ *   act[m, f]  = silu(h[m, f]) * h[m, F + f]      [M, F],  dtype
+ * a [M, K], b [E, K, 2F] with the gate columns [0, F) and the up columns
+ * [F, 2F); offsets as above.  act is computed from the stored h values
+ * (rounded to dtype first), so the result is the one moe_grouped_gemm_fwd
+ * followed by moe_act_fwd gives -- which is also what this call runs for
+ * shapes and dtypes that the bf16 MFMA path does not take.  h is still
+ * written because the backward pass reads it.  F must be a multiple of 8
+ * (MOE_ERR_UNSUPPORTED); on the MFMA path every pointer must be 16-byte
+ * aligned (MOE_ERR_INVALID_ARG).  Rows outside every group are left
+ * untouched.
+ */
+moe_status moe_grouped_gemm_swiglu_fwd(const void* a, const void* b,
+                                       const int32_t* offsets, int M, int K,
+                                       int F, int E, moe_dtype dtype, void* h,
+                                       void* act, moe_stream_t stream);
 
 /*
  * moe_act_fwd -- SwiGLU activation [Summary, Method details / key design:

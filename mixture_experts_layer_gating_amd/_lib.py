@@ -34,7 +34,8 @@ SYMBOLS = (
     "moe_count_index_workspace_size", "moe_count_index", "moe_permute",
     "moe_unpermute", "moe_unpermute_bwd", "moe_grouped_gemm_workspace_size",
     "moe_grouped_gemm_plan",
-    "moe_grouped_gemm_fwd", "moe_grouped_gemm_bwd", "moe_act_fwd", "moe_act_bwd",
+    "moe_grouped_gemm_fwd", "moe_grouped_gemm_bwd", "moe_grouped_gemm_swiglu_fwd",
+    "moe_act_fwd", "moe_act_bwd",
 )
 
 
@@ -94,6 +95,7 @@ _SIG = {
     "moe_grouped_gemm_plan": ([_i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p], _i),
     "moe_grouped_gemm_fwd": ([_p, _p, _p, _i, _i, _i, _i, _i, _p, _i, _p, _z, _p], _i),
     "moe_grouped_gemm_bwd": ([_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _z, _p], _i),
+    "moe_grouped_gemm_swiglu_fwd": ([_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p], _i),
     "moe_act_fwd": ([_p, _i, _i, _i, _p, _p], _i),
     "moe_act_bwd": ([_p, _p, _i, _i, _i, _p, _p], _i),
 }
@@ -215,6 +217,11 @@ def moe_grouped_gemm_bwd(a, b, dc, offsets, M, K, N, E, dtype, da, da_add, db, w
     _check(_lib.moe_grouped_gemm_bwd(_ptr(a), _ptr(b), _ptr(dc), _ptr(offsets), M, K, N, E,
                                      dtype, _ptr(da), _ptr(da_add), _ptr(db), _ptr(ws), ws_bytes,
                                      _stream(stream, dc)))
+
+
+def moe_grouped_gemm_swiglu_fwd(a, b, offsets, M, K, F, E, dtype, h, act, stream=None):
+    _check(_lib.moe_grouped_gemm_swiglu_fwd(_ptr(a), _ptr(b), _ptr(offsets), M, K, F, E, dtype,
+                                            _ptr(h), _ptr(act), _stream(stream, a)))
 
 
 def moe_act_fwd(h, M, F, dtype, a, stream=None):

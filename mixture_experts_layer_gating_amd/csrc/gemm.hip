@@ -25,6 +25,8 @@
 //
 // Float32 (and shapes whose K or N is not a multiple of 8) run on a plain
 // LDS-tiled FMA kernel with the same tile resolution.
+#include <math.h>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -46,6 +48,7 @@ struct GemmArgs {
   int ntm;    // TN: row tiles over K
   int ntn;    // column tiles
   int split;  // TN: reduction slices (partials written to out as [split][E][K][N])
+  void* out2;  // NN with the SwiGLU epilogue: act [M, N / 2]
 };
 
 // ------------------------------------------------------------------ tiles
@@ -276,7 +279,12 @@ __device__ __forceinline__ int swz_t(int k) {
 struct Operand {
   const uint16_t* base;
   long long ld;
-  int o_valid;  // number of valid o from the tile's first one
+  int o_valid;  // number of valid o from the tile's first one (glu: hidden units)
+  // SwiGLU weights [K, 2F]: tile column o is hidden unit f = (o / 64) * 32 +
+  // o % 32 of the gate half (o / 32 even) or of the up half (o / 32 odd),
+  // i.e. memory column (o / 32 % 2) * glu_f + glu_j0 + f.  glu_f = 0: plain.
+  int glu_f;
+  int glu_j0;
 };
 
 // Loads of one operand, shared by the NW waves of the workgroup.  A k-strided
@@ -321,8 +329,16 @@ struct DmaLoader {
         // which is below 2^31 bytes).
         const int row = pos / (O * 2);
         const int u = ((pos % (O * 2)) / 16) ^ swz_t<O>(row);
-        voff[q] = (u * 8 + 8 <= op.o_valid) ? static_cast<unsigned>((row * op.ld + u * 8) * 2)
-                                            : kOOB;
+        int col = u * 8;
+        bool valid;
+        if (op.glu_f) {
+          const int blk = col >> 5, f = (blk >> 1) * 32 + (col & 31);
+          valid = f + 8 <= op.o_valid;
+          col = (blk & 1) * op.glu_f + op.glu_j0 + f;
+        } else {
+          valid = col + 8 <= op.o_valid;
+        }
+        voff[q] = valid ? static_cast<unsigned>((row * op.ld + col) * 2) : kOOB;
       }
     }
     if constexpr (!STRIDED) {
@@ -511,13 +527,19 @@ __device__ __forceinline__ void reduce_tile(f32x16 (&acc)[MI][NI], const XL& xl,
 }
 
 // Workgroup: WGM x WGN waves, each computing a (BM / WGM) x (BN / WGN) piece.
-template <int MODE, int BM, int BN, int WGM, int WGN, typename OutT>
+// GLU (NN, bf16): the SwiGLU variant of GEMM 1 -- the tile's columns are
+// interleaved 32-column blocks of gate and up weights for 128 hidden units
+// (see Operand), so every wave holds the gate and the up value of the same
+// units in the same lanes; the epilogue stores h and act = silu(g) * u.
+template <int MODE, int BM, int BN, int WGM, int WGN, typename OutT, bool GLU = false>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p) {
   constexpr bool XS = (MODE == kTN);  // x operand k-strided in memory
   constexpr bool YS = (MODE != kNT);  // y operand k-strided in memory
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int MI = WM / 32, NI = WN / 32;
+  static_assert(!GLU || (MODE == kNN && NI == 2 && sizeof(OutT) == 2),
+                "the SwiGLU epilogue pairs a wave's two column blocks");
   // Elements per buffer: four quad buffers (k-strided) or two pair buffers.
   constexpr int XBE = XS ? BM * kBK : BM * 2 * kBK;
   constexpr int YBE = YS ? BN * kBK : BN * 2 * kBK;
@@ -544,24 +566,29 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
   t.r_hi = __builtin_amdgcn_readfirstlane(t.r_hi);
   t.g0 = __builtin_amdgcn_readfirstlane(t.g0);
   t.g1 = __builtin_amdgcn_readfirstlane(t.g1);
-  const int j0 = t.j0 * BN;
+  const int j0 = t.j0 * (GLU ? BN / 2 : BN);  // GLU: first hidden unit of the tile
   const long long KN = static_cast<long long>(p.K) * p.N;
 
-  Operand xo, yo;
-  if constexpr (MODE == kNN) {
+  Operand xo{}, yo{};
+  if constexpr (GLU) {
+    const int F = p.N / 2;
     xo = {static_cast<const uint16_t*>(p.x) + static_cast<long long>(t.i0) * p.K, p.K,
-          t.g1 - t.i0};
-    yo = {static_cast<const uint16_t*>(p.y) + t.e * KN + j0, p.N, p.N - j0};
+          t.g1 - t.i0, 0, 0};
+    yo = {static_cast<const uint16_t*>(p.y) + t.e * KN, p.N, F - j0, F, j0};
+  } else if constexpr (MODE == kNN) {
+    xo = {static_cast<const uint16_t*>(p.x) + static_cast<long long>(t.i0) * p.K, p.K,
+          t.g1 - t.i0, 0, 0};
+    yo = {static_cast<const uint16_t*>(p.y) + t.e * KN + j0, p.N, p.N - j0, 0, 0};
   } else if constexpr (MODE == kNT) {
     xo = {static_cast<const uint16_t*>(p.x) + static_cast<long long>(t.i0) * p.N, p.N,
-          t.g1 - t.i0};
+          t.g1 - t.i0, 0, 0};
     yo = {static_cast<const uint16_t*>(p.y) + t.e * KN + static_cast<long long>(j0) * p.N, p.N,
-          p.K - j0};
+          p.K - j0, 0, 0};
   } else {
     xo = {static_cast<const uint16_t*>(p.x) + static_cast<long long>(t.r_lo) * p.K + t.i0, p.K,
-          p.K - t.i0};
+          p.K - t.i0, 0, 0};
     yo = {static_cast<const uint16_t*>(p.y) + static_cast<long long>(t.r_lo) * p.N + j0, p.N,
-          p.N - j0};
+          p.N - j0, 0, 0};
   }
   DmaLoader<XS, BM, NW> xl;
   DmaLoader<YS, BN, NW> yl;
@@ -608,6 +635,31 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
       MOE_REDUCE(0);
     }
 #undef MOE_REDUCE
+  }
+
+  if constexpr (GLU) {
+    // acc[i][0]: gate, acc[i][1]: up, of hidden unit j0 + wn * 32 + l % 32.
+    // act is computed from the stored (bf16) h values, as the separate
+    // activation kernel does.
+    const int F = p.N / 2;
+    const int f = j0 + wn * 32 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ra = t.i0 + wm * WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (ra < t.g1 && f < F) {
+          const uint16_t gb = f32_to_bf16(acc[i][0][r]), ub = f32_to_bf16(acc[i][1][r]);
+          uint16_t* hr = static_cast<uint16_t*>(p.out) + static_cast<long long>(ra) * p.N;
+          hr[f] = gb;
+          hr[F + f] = ub;
+          const float g = bf16_to_f32(gb), u = bf16_to_f32(ub);
+          static_cast<uint16_t*>(p.out2)[static_cast<long long>(ra) * F + f] =
+              f32_to_bf16(g * (1.f / (1.f + expf(-g))) * u);
+        }
+      }
+    }
+    return;
   }
 
   // Epilogue.  32x32 accumulator layout: lane l, register r holds
@@ -835,10 +887,10 @@ bool mfma_ok(moe_dtype dt, int M, int K, int N) {
 // 16-byte boundaries (null pointers pass).
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; }
 
-template <int MODE, int BM, int BN, int WGM, int WGN, typename OutT>
+template <int MODE, int BM, int BN, int WGM, int WGN, typename OutT, bool GLU = false>
 void launch_mfma(GemmArgs p, long long tiles_upper, hipStream_t st) {
   const long long grid = ceil_div(tiles_upper, 8) * 8;
-  hipLaunchKernelGGL((gemm_mfma_kernel<MODE, BM, BN, WGM, WGN, OutT>),
+  hipLaunchKernelGGL((gemm_mfma_kernel<MODE, BM, BN, WGM, WGN, OutT, GLU>),
                      dim3(static_cast<unsigned>(grid)), dim3(64 * WGM * WGN), 0, st, p);
 }
 
@@ -857,6 +909,24 @@ void dispatch_mfma(Cfg c, GemmArgs p, hipStream_t st) {
   else if (c.bm == 128 && c.bn == 128) launch_mfma<MODE, 128, 128, 2, 2, OutT>(p, upper, st);
   else if (c.bm == 64 && c.bn == 256) launch_mfma<MODE, 64, 256, 1, 4, OutT>(p, upper, st);
   else launch_mfma<MODE, 64, 64, 2, 2, OutT>(p, upper, st);
+}
+
+// GEMM 1 with the SwiGLU epilogue: tiles of 128 hidden units (gate and up
+// columns interleaved), which needs two 32-column blocks per wave.
+Cfg pick_glu_cfg(int M, int E, int N) {
+  const Cfg c = pick_row_cfg(M, E, N);
+  return c.bn == 64 ? Cfg{128, 128} : c;
+}
+
+void dispatch_glu(Cfg c, GemmArgs p, hipStream_t st) {
+  p.ntn = static_cast<int>(ceil_div(p.N / 2, c.bn / 2));
+  const long long upper = (ceil_div(p.M, c.bm) + p.E) * p.ntn;
+  if (c.bm == 256 && c.bn == 256)
+    launch_mfma<kNN, 256, 256, 2, 4, uint16_t, true>(p, upper, st);
+  else if (c.bm == 64 && c.bn == 256)
+    launch_mfma<kNN, 64, 256, 1, 4, uint16_t, true>(p, upper, st);
+  else
+    launch_mfma<kNN, 128, 128, 2, 2, uint16_t, true>(p, upper, st);
 }
 
 template <int MODE, typename InT, typename OutT>
@@ -904,8 +974,8 @@ extern "C" moe_status moe_grouped_gemm_plan(int product, int M, int K, int N, in
                                             moe_dtype dtype, int* tile_m, int* tile_n,
                                             int* waves_m, int* waves_n, int* split, int* mfma) {
   clear_error();
-  MOE_REQUIRE(product >= 0 && product <= 2, MOE_ERR_INVALID_ARG,
-              "moe_grouped_gemm_plan: product must be 0, 1 or 2");
+  MOE_REQUIRE(product >= 0 && product <= 3, MOE_ERR_INVALID_ARG,
+              "moe_grouped_gemm_plan: product must be 0, 1, 2 or 3");
   MOE_REQUIRE(M >= 1 && K >= 1 && N >= 1 && E >= 1, MOE_ERR_INVALID_ARG,
               "moe_grouped_gemm_plan: sizes must be >= 1");
   MOE_REQUIRE(dtype_ok(dtype), MOE_ERR_UNSUPPORTED, "moe_grouped_gemm_plan: unknown dtype");
@@ -914,6 +984,7 @@ extern "C" moe_status moe_grouped_gemm_plan(int product, int M, int K, int N, in
   int s = 1;
   if (m) {
     if (product == 0) c = pick_row_cfg(M, E, N);
+    else if (product == 3) c = pick_glu_cfg(M, E, N);
     else if (product == 1) c = pick_row_cfg(M, E, K);
     else {
       c = pick_tn_cfg(K, N, E);
@@ -933,6 +1004,33 @@ extern "C" moe_status moe_grouped_gemm_plan(int product, int M, int K, int N, in
   if (split) *split = s;
   if (mfma) *mfma = m ? 1 : 0;
   return MOE_OK;
+}
+
+extern "C" moe_status moe_grouped_gemm_swiglu_fwd(const void* a, const void* b,
+                                                  const int32_t* offsets, int M, int K, int F,
+                                                  int E, moe_dtype dtype, void* h, void* act,
+                                                  moe_stream_t stream) {
+  clear_error();
+  MOE_REQUIRE(F >= 1 && F <= (1 << 29), MOE_ERR_INVALID_ARG,
+              "moe_grouped_gemm_swiglu_fwd: F out of range");
+  const int N = 2 * F;
+  if (moe_status s = check_gemm(offsets, M, K, N, E, dtype)) return s;
+  MOE_REQUIRE(a && b && h && act, MOE_ERR_INVALID_ARG, "moe_grouped_gemm_swiglu_fwd: null pointer");
+  MOE_REQUIRE(F % 8 == 0, MOE_ERR_UNSUPPORTED,
+              "moe_grouped_gemm_swiglu_fwd: F must be a multiple of 8");
+  if (mfma_ok(dtype, M, K, N)) {
+    MOE_REQUIRE(aligned16(a) && aligned16(b) && aligned16(h) && aligned16(act),
+                MOE_ERR_INVALID_ARG,
+                "moe_grouped_gemm_swiglu_fwd: bf16 operands and results must be 16-byte aligned");
+    GemmArgs p{a, b, nullptr, h, offsets, M, K, N, E, 0, 0, 1, act};
+    dispatch_glu(pick_glu_cfg(M, E, N), p, as_stream(stream));
+    return check_launch("moe_grouped_gemm_swiglu_fwd");
+  }
+  // Shapes the MFMA path does not take: the GEMM, then the activation kernel.
+  if (moe_status s = moe_grouped_gemm_fwd(a, b, offsets, M, K, N, E, dtype, h, dtype, nullptr, 0,
+                                          stream))
+    return s;
+  return moe_act_fwd(h, M, F, dtype, act, stream);
 }
 
 extern "C" moe_status moe_grouped_gemm_fwd(const void* a, const void* b, const int32_t* offsets,

@@ -14,8 +14,9 @@ method]):
     idx, w, p = top-k softmax          moe_route_topk
     counts, offsets, dest, src         moe_count_index
     xp[dest] = x (xp = x[src // k])    moe_permute
-    h  = xp @ W1[e]                    moe_grouped_gemm_fwd
-    a  = silu(h_gate) * h_up           moe_act_fwd
+    h  = xp @ W1[e]                    moe_grouped_gemm_swiglu_fwd (one launch;
+    a  = silu(h_gate) * h_up             with fuse_act=False: moe_grouped_gemm_fwd
+                                         then moe_act_fwd)
     yp = a @ W2[e]                     moe_grouped_gemm_fwd
     y  = sum_j w * yp[dest]            moe_unpermute
 
@@ -53,13 +54,15 @@ class MoELayer:
     next call.
     """
 
-    def __init__(self, T, d, E, k, F, dtype=torch.bfloat16, device="cuda", renorm=False):
+    def __init__(self, T, d, E, k, F, dtype=torch.bfloat16, device="cuda", renorm=False,
+                 fuse_act=True):
         if not (1 <= k <= E):
             raise ValueError("need 1 <= k <= E")
         self.T, self.d, self.E, self.k, self.F = T, d, E, k, F
         self.dtype = dtype
         self.code = L.dtype_code(dtype)
         self.renorm = bool(renorm)
+        self.fuse_act = bool(fuse_act)
         self.device = torch.device(device)
         Tk = T * k
         self.Tk = Tk
@@ -126,11 +129,16 @@ class MoELayer:
                               self.ci_ws, self.ci_ws.numel(), stream=s)
         with self._span("permute"):
             L.moe_permute(x, self.dest, T, k, d, c, self.xp, stream=s)
-        with self._span("gemm1_fwd"):
-            L.moe_grouped_gemm_fwd(self.xp, w1, self.offsets, Tk, d, 2 * F, E, c, self.h, c,
-                                   stream=s)
-        with self._span("act_fwd"):
-            L.moe_act_fwd(self.h, Tk, F, c, self.a, stream=s)
+        if self.fuse_act:
+            with self._span("gemm1_swiglu_fwd"):
+                L.moe_grouped_gemm_swiglu_fwd(self.xp, w1, self.offsets, Tk, d, F, E, c, self.h,
+                                              self.a, stream=s)
+        else:
+            with self._span("gemm1_fwd"):
+                L.moe_grouped_gemm_fwd(self.xp, w1, self.offsets, Tk, d, 2 * F, E, c, self.h, c,
+                                       stream=s)
+            with self._span("act_fwd"):
+                L.moe_act_fwd(self.h, Tk, F, c, self.a, stream=s)
         with self._span("gemm2_fwd"):
             L.moe_grouped_gemm_fwd(self.a, w2, self.offsets, Tk, F, d, E, c, self.yp, c,
                                    stream=s)

@@ -83,6 +83,14 @@ def test_gemm_validation_and_workspace():
     assert _rc("moe_grouped_gemm_fwd", FAKE, FAKE, FAKE, 0, 8, 8, 1, L.MOE_BF16, FAKE, L.MOE_BF16, None, 0, None) == L.MOE_ERR_INVALID_ARG
     assert _rc("moe_grouped_gemm_bwd", FAKE, FAKE, FAKE, FAKE, 8192, 2048, 64, 1, L.MOE_BF16, None, None, FAKE, None, 0, None) == L.MOE_ERR_WORKSPACE
     assert _rc("moe_grouped_gemm_bwd", FAKE, None, FAKE, FAKE, 16, 8, 8, 1, L.MOE_BF16, FAKE, None, None, None, 0, None) == L.MOE_ERR_INVALID_ARG
+    # fused GEMM 1 + SwiGLU
+    assert _rc("moe_grouped_gemm_swiglu_fwd", FAKE, FAKE, FAKE, 16, 8, 12, 1, L.MOE_BF16, FAKE, FAKE, None) == L.MOE_ERR_UNSUPPORTED
+    assert _rc("moe_grouped_gemm_swiglu_fwd", FAKE, FAKE, FAKE, 16, 8, 16, 1, L.MOE_BF16, None, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert _rc("moe_grouped_gemm_swiglu_fwd", FAKE, FAKE, None, 16, 8, 16, 1, L.MOE_BF16, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert _rc("moe_grouped_gemm_swiglu_fwd", FAKE, FAKE, FAKE, 16, 8, 0, 1, L.MOE_BF16, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert _rc("moe_grouped_gemm_swiglu_fwd", FAKE, FAKE, FAKE, 16, 8, 16, 1, L.MOE_BF16, FAKE, FAKE + 8, None) == L.MOE_ERR_INVALID_ARG
+    assert L.moe_grouped_gemm_plan(3, 65536, 2048, 2048, 64, L.MOE_BF16)["tile_n"] == 256
+    assert L.moe_grouped_gemm_plan(3, 2048, 512, 64, 1, L.MOE_BF16)["tile_n"] == 128
     # the MFMA path moves 16-byte vectors: misaligned operands are rejected
     odd = FAKE + 8
     assert _rc("moe_grouped_gemm_fwd", odd, FAKE, FAKE, 4, 8, 8, 1, L.MOE_BF16, FAKE, L.MOE_BF16, None, 0, None) == L.MOE_ERR_INVALID_ARG

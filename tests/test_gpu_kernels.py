@@ -216,3 +216,41 @@ def test_grouped_gemm_split_weight_grad():
     torch.cuda.synchronize()
     _, rdb = O.grouped_matmul_backward(a, b, dc, off)
     assert rel(host(db), rdb) <= TOL_F32
+
+
+# ------------------------------------------------------------------ GEMM 1 + SwiGLU (fused)
+SWIGLU_CASES = [
+    # M, K, F, E, pattern, dtype
+    (16384, 256, 1024, 8, "random", "bf16"),   # 256x256 tiles
+    (1000, 256, 200, 5, "empty", "bf16"),      # 128x128 tiles, F not a multiple of 128
+    (300, 512, 384, 40, "random", "bf16"),     # small groups: 64x256 tiles
+    (2048, 512, 32, 1, "uniform", "bf16"),     # 64-column shape, run on 128x128 tiles
+    (4096, 200, 136, 3, "skew", "bf16"),       # K not a multiple of 64
+    (333, 12, 24, 3, "random", "bf16"),        # K not a multiple of 8 -> GEMM + activation
+    (129, 40, 24, 3, "random", "fp32"),        # float32 -> GEMM + activation
+]
+
+
+@pytest.mark.parametrize("M,K,F,E,pattern,dtype", SWIGLU_CASES)
+def test_grouped_gemm_swiglu(M, K, F, E, pattern, dtype):
+    say(f"grouped_gemm_swiglu M={M} K={K} F={F} E={E} {pattern} {dtype}")
+    tdt = DTYPES[dtype]
+    code = L.dtype_code(tdt)
+    off = _groups(M, E, pattern, 7)
+    a = _normal((M, K), 21, dtype=dtype)
+    b = _normal((E, K, 2 * F), 22, scale=0.05, dtype=dtype)
+    ad, bd, offd = dev(a, tdt), dev(b, tdt), dev(off)
+    h = torch.zeros(M, 2 * F, dtype=tdt, device=DEV)
+    act = torch.zeros(M, F, dtype=tdt, device=DEV)
+    L.moe_grouped_gemm_swiglu_fwd(ad, bd, offd, M, K, F, E, code, h, act)
+    # the unfused reference on the device: the activation kernel on the fused h
+    act2 = torch.zeros(M, F, dtype=tdt, device=DEV)
+    L.moe_act_fwd(h, M, F, code, act2)
+    torch.cuda.synchronize()
+    rows = slice(0, int(off[-1]))
+    ref_h = O.grouped_matmul(a, b, off)
+    tol = TOL_ONE_ROUNDING if dtype == "bf16" else TOL_F32
+    assert rel(host(h)[rows], ref_h[rows]) <= tol
+    # act is computed from the stored h: exactly what the activation kernel gives
+    np.testing.assert_array_equal(bits(act)[rows], bits(act2)[rows])
+    assert rel(host(act)[rows], O.swiglu(ref_h)[rows]) <= 2 * tol

@@ -24,11 +24,12 @@ def _native_lib():
     import mixture_experts_layer_gating_amd._lib  # noqa: F401  (raises if not built)
 
 
-def _run(inp, renorm=False):
+def _run(inp, renorm=False, fuse_act=True):
     from mixture_experts_layer_gating_amd.layer import MoELayer
     wl = inp.wl
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-    layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, dtype=tdt, device=DEV, renorm=renorm)
+    layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, dtype=tdt, device=DEV, renorm=renorm,
+                     fuse_act=fuse_act)
     x, wr, w1, w2, dy = (dev(a, tdt) for a in (inp.x, inp.wr, inp.w1, inp.w2, inp.dy))
     bias = None if inp.bias is None else dev(inp.bias)
     forced = None if inp.forced_idx is None else dev(inp.forced_idx)
@@ -156,3 +157,21 @@ def test_layer_full_size_sampled(name):
     # empty experts have exactly zero weight gradients
     for e in np.flatnonzero(counts == 0)[:4]:
         assert not host(g.dw2[int(e)]).any()
+
+
+def test_layer_fused_activation_matches_unfused():
+    """GEMM 1 with the SwiGLU epilogue gives the same bits as GEMM 1 followed
+    by the activation kernel, through the whole forward and backward."""
+    wl = Workload("fuse", T=1024, d=512, E=8, k=2, F=384, dtype="bf16", w_std=0.05, seed=31)
+    say(f"layer fused vs unfused {wl}")
+    inp = make_inputs(wl)
+    la, ga, _ = _run(inp, fuse_act=True)
+    ya, ha, aa = (host(t).copy() for t in (la.y, la.h, la.a))
+    da = {k: host(getattr(ga, k)).copy() for k in ("dx", "dwr", "dw1", "dw2")}
+    lb, gb, _ = _run(inp, fuse_act=False)
+    rows = slice(0, wl.T * wl.k)
+    np.testing.assert_array_equal(ha[rows], host(lb.h)[rows])
+    np.testing.assert_array_equal(aa[rows], host(lb.a)[rows])
+    np.testing.assert_array_equal(ya, host(lb.y))
+    for k, v in da.items():
+        np.testing.assert_array_equal(v, host(getattr(gb, k)), err_msg=k)
