@@ -22,9 +22,10 @@ method]):
 
 Backward of <y, dy> (the forward-plus-backward unit of [Brief, Key results]):
 
-    dyp, dw   moe_unpermute_bwd           da, dW2   moe_grouped_gemm_bwd
-    dh        moe_act_bwd                 dxp, dW1  moe_grouped_gemm_bwd
-    dx_e      moe_unpermute (w = NULL)    dlogits   moe_route_topk_bwd
+    dyp, dw   moe_unpermute_bwd           da        moe_grouped_gemm_bwd
+    dh        moe_act_bwd                 dW2       moe_grouped_gemm_bwd
+    dxp       moe_grouped_gemm_bwd        dx_e      moe_unpermute (w = NULL)
+    dW1       moe_grouped_gemm_bwd        dlogits   moe_route_topk_bwd
     dx = dx_e + dlogits @ wr^T, dwr = x^T @ dlogits   moe_grouped_gemm_bwd
 """
 from __future__ import annotations
@@ -160,19 +161,23 @@ class MoELayer:
         with self._span("gemm2_bwd_da"):
             L.moe_grouped_gemm_bwd(self.a, w2, self.dyp, self.offsets, Tk, F, d, E, c, self.da,
                                    None, None, ws, wsb, stream=s)
+        # Each product is consumed right after it is made (da by the activation
+        # backward, dxp by the permutation backward), while it is still in the
+        # last-level cache; the weight gradients, which stream the most data,
+        # come after.
+        with self._span("act_bwd"):
+            L.moe_act_bwd(self.h, self.da, Tk, F, c, self.dh, stream=s)
         with self._span("gemm2_bwd_dw"):
             L.moe_grouped_gemm_bwd(self.a, w2, self.dyp, self.offsets, Tk, F, d, E, c, None,
                                    None, self.dw2, ws, wsb, stream=s)
-        with self._span("act_bwd"):
-            L.moe_act_bwd(self.h, self.da, Tk, F, c, self.dh, stream=s)
         with self._span("gemm1_bwd_da"):
             L.moe_grouped_gemm_bwd(self.xp, w1, self.dh, self.offsets, Tk, d, 2 * F, E, c,
                                    self.dxp, None, None, ws, wsb, stream=s)
+        with self._span("permute_bwd"):
+            L.moe_unpermute(self.dxp, self.dest, None, T, k, d, c, self.dx_e, stream=s)
         with self._span("gemm1_bwd_dw"):
             L.moe_grouped_gemm_bwd(self.xp, w1, self.dh, self.offsets, Tk, d, 2 * F, E, c, None,
                                    None, self.dw1, ws, wsb, stream=s)
-        with self._span("permute_bwd"):
-            L.moe_unpermute(self.dxp, self.dest, None, T, k, d, c, self.dx_e, stream=s)
         with self._span("route_topk_bwd"):
             L.moe_route_topk_bwd(self.probs, self.idx, self.dw, T, E, k, self.renorm,
                                  self.dlogits, c, stream=s)
