@@ -154,15 +154,27 @@ struct TileInfo {
 };
 
 // Returns false if this workgroup has no tile.  Must be called by all threads.
+constexpr int kTnDeal = 2;  // weight-gradient tile rows dealt to an XCD at a time
+
 template <int MODE, int BM>
 __device__ bool resolve_tile(const GemmArgs& p, int* sh, TileInfo& t) {
   if constexpr (MODE == kTN) {
+    // Tile rows (slice, e, row tile) are dealt over the XCDs in pairs --
+    // XCD x takes rows 2x, 2x + 1, 2x + 16, 2x + 17, ... with all ntn column
+    // tiles of each -- so every XCD gets a share of every group however
+    // unevenly the rows are spread over the groups (the reduction of a big
+    // group is as long as its row count), while each group's column operand
+    // is read by a few XCDs only.  (Single rows balance a skewed routing
+    // slightly better but cost the even one more L2 traffic; groups of four
+    // balance worse.)
     const long long per_e = static_cast<long long>(p.ntm) * p.ntn;
-    const long long n_act = per_e * p.E * p.split;
-    const long long per = (n_act + 7) / 8;
+    const long long nrows = static_cast<long long>(p.ntm) * p.E * p.split;
     const long long rank = blockIdx.x >> 3;
-    const long long L = static_cast<long long>(blockIdx.x & 7) * per + rank;
-    if (rank >= per || L >= n_act) return false;
+    const long long gsz = static_cast<long long>(kTnDeal) * p.ntn;
+    const long long within = rank % gsz;
+    const long long R = ((rank / gsz) * 8 + (blockIdx.x & 7)) * kTnDeal + within / p.ntn;
+    if (R >= nrows) return false;
+    const long long L = R * p.ntn + within % p.ntn;
     const long long per_slice = per_e * p.E;
     t.slice = static_cast<int>(L / per_slice);
     const long long rem0 = L - static_cast<long long>(t.slice) * per_slice;
@@ -900,8 +912,10 @@ void dispatch_mfma(Cfg c, GemmArgs p, hipStream_t st) {
   p.ntn = static_cast<int>(ceil_div(ncols, c.bn));
   long long upper;
   if (MODE == kTN) {
+    // 8 XCDs x (tile rows per XCD, whole deals) x ntn
     p.ntm = static_cast<int>(ceil_div(p.K, c.bm));
-    upper = static_cast<long long>(p.ntm) * p.ntn * p.E * p.split;
+    upper = ceil_div(static_cast<long long>(p.ntm) * p.E * p.split, 8 * kTnDeal) * 8 * kTnDeal *
+            p.ntn;
   } else {
     upper = (ceil_div(p.M, c.bm) + p.E) * p.ntn;
   }
@@ -936,8 +950,9 @@ void launch_simt(GemmArgs p, hipStream_t st) {
   p.split = 1;
   long long upper;
   if (MODE == kTN) {
+    // 8 XCDs x (tile rows per XCD, whole deals) x ntn
     p.ntm = static_cast<int>(ceil_div(p.K, kSimtTile));
-    upper = static_cast<long long>(p.ntm) * p.ntn * p.E;
+    upper = ceil_div(static_cast<long long>(p.ntm) * p.E, 8 * kTnDeal) * 8 * kTnDeal * p.ntn;
   } else {
     upper = (ceil_div(p.M, kSimtTile) + p.E) * p.ntn;
   }
