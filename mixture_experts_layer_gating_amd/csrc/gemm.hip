@@ -27,6 +27,8 @@
 // LDS-tiled FMA kernel with the same tile resolution.
 #include <math.h>
 
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -678,42 +680,78 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
   // row (r/4)*8 + (l/32)*4 + r%4, column l%32.  Consecutive lanes write
   // consecutive columns, so each store instruction covers two 64-byte row
   // segments (bf16).  (Whole-tile stores leave every compute unit at once;
-  // wider per-lane stores only make that burst denser.)
-#pragma unroll
-  for (int i = 0; i < MI; ++i) {
+  // wider per-lane stores only make that burst denser.)  The stores go
+  // through a buffer descriptor over the tile's valid rows, so rows past the
+  // group (or past K) fall outside it and the hardware drops them; a lane
+  // whose column is past the matrix gets an out-of-range offset.  Offsets
+  // are 32-bit: row and column constants fold into scalar registers, and no
+  // store needs a branch.
+  {
+    constexpr int SZ = sizeof(OutT);
+    const int ld = (MODE == kNT) ? p.K : p.N;  // output row length
+    const int row_end = (MODE == kTN) ? p.K : t.g1;
+    const int rows = min(BM, row_end - t.i0);
+    long long first;  // element index of the tile's (0, 0)
+    if constexpr (MODE == kTN)
+      first = (static_cast<long long>(t.slice) * p.E + t.e) * KN +
+              static_cast<long long>(t.i0) * p.N + j0;
+    else
+      first = static_cast<long long>(t.i0) * ld + j0;
+    const __amdgpu_buffer_rsrc_t out_rs =
+        make_rsrc(static_cast<char*>(p.out) + first * SZ,
+                  (static_cast<long long>(rows) * ld - j0) * SZ);
+    // NT addend (or an empty range when there is none; never read then)
+    const __amdgpu_buffer_rsrc_t add_rs =
+        make_rsrc(MODE == kNT && p.add ? static_cast<const char*>(p.add) + first * 2
+                                       : static_cast<const char*>(p.out),
+                  MODE == kNT && p.add ? (static_cast<long long>(rows) * ld - j0) * 2 : 0);
+    // Per lane and column block: its byte offset in the tile, or kOOB; the
+    // row's offset (a multiple of the row length, below 2^31) is added to it,
+    // which keeps kOOB-based offsets out of range.
+    unsigned col_off[NI];
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int col = wn * WN + j * 32 + (lane & 31);
+      col_off[j] = j0 + col < ld
+                       ? static_cast<unsigned>(((wm * WM + (lane >> 5) * 4) * ld + col) * SZ)
+                       : kOOB;
+    }
+    // The stores, with the (NT) addend read from the same offsets.
+    auto store_all = [&](auto with_add) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        float v = acc[i][j][r];
-        if constexpr (MODE == kNN) {
-          const int ra = t.i0 + row, ca = j0 + col;
-          if (ra < t.g1 && ca < p.N) {
-            const long long o = static_cast<long long>(ra) * p.N + ca;
-            if constexpr (sizeof(OutT) == 2)
-              static_cast<uint16_t*>(p.out)[o] = f32_to_bf16(v);
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          // A block's addend values are all read before any of its stores
+          // (the compiler cannot move a read across a possibly aliasing store).
+          float addv[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row_c = i * 32 + (r >> 2) * 8 + (r & 3);
+            const unsigned off = col_off[j] + static_cast<unsigned>(row_c * ld * SZ);
+            addv[r] = 0.f;
+            if constexpr (decltype(with_add)::value)
+              addv[r] = bf16_to_f32(static_cast<uint16_t>(
+                  __builtin_amdgcn_raw_buffer_load_b16(add_rs, off, 0, 0)));
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row_c = i * 32 + (r >> 2) * 8 + (r & 3);
+            const unsigned off = col_off[j] + static_cast<unsigned>(row_c * ld * SZ);
+            float v = acc[i][j][r];
+            if constexpr (decltype(with_add)::value) v += addv[r];
+            if constexpr (SZ == 2)
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), out_rs, off, 0, 0);
             else
-              static_cast<float*>(p.out)[o] = v;
-          }
-        } else if constexpr (MODE == kNT) {
-          const int ra = t.i0 + row, ca = j0 + col;
-          if (ra < t.g1 && ca < p.K) {
-            const long long o = static_cast<long long>(ra) * p.K + ca;
-            if (p.add) v += bf16_to_f32(static_cast<const uint16_t*>(p.add)[o]);
-            static_cast<uint16_t*>(p.out)[o] = f32_to_bf16(v);
-          }
-        } else {
-          const int ra = t.i0 + row, ca = j0 + col;
-          if (ra < p.K && ca < p.N) {
-            const long long o = (static_cast<long long>(t.slice) * p.E + t.e) * KN +
-                                static_cast<long long>(ra) * p.N + ca;
-            static_cast<float*>(p.out)[o] = v;
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), out_rs, off, 0, 0);
           }
         }
       }
-    }
+    };
+    if (MODE == kNT && p.add)
+      store_all(std::true_type{});
+    else
+      store_all(std::false_type{});
   }
 }
 
