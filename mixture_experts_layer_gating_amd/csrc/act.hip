@@ -50,7 +50,7 @@ __device__ __forceinline__ void store_f32(T* p, const float* f) {
   *reinterpret_cast<V16*>(p) = v;
 }
 
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.f / (1.f + expf(-z)); }
+
 
 // Flat 32-bit index over (row, 16-byte chunk of the gate half), one chunk per
 // thread per grid-stride step.
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kActBlock) void act_fwd_kernel(const T* __restrict_
     load_f32(hr, g);
     load_f32(hr + F, u);
 #pragma unroll
-    for (int e = 0; e < N; ++e) o[e] = g[e] * sigmoidf_(g[e]) * u[e];
+    for (int e = 0; e < N; ++e) o[e] = g[e] * sigmoid_fast(g[e]) * u[e];
     store_f32(a + static_cast<size_t>(m) * F + c * N, o);
   }
 }
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kActBlock) void act_bwd_kernel(const T* __restrict_
     load_f32(da + static_cast<size_t>(m) * F + c * N, d);
 #pragma unroll
     for (int e = 0; e < N; ++e) {
-      const float s = sigmoidf_(g[e]);
+      const float s = sigmoid_fast(g[e]);
       dg[e] = d[e] * u[e] * s * (1.f + g[e] * (1.f - s));
       du[e] = d[e] * g[e] * s;
     }

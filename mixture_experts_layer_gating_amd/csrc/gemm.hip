@@ -654,23 +654,34 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
   if constexpr (GLU) {
     // acc[i][0]: gate, acc[i][1]: up, of hidden unit j0 + wn * 32 + l % 32.
     // act is computed from the stored (bf16) h values, as the separate
-    // activation kernel does.
+    // activation kernel does.  Stores go through buffer descriptors over the
+    // tile's valid rows of h and act (rows past the group are dropped); a
+    // lane past the last hidden unit starts from an out-of-range offset.
     const int F = p.N / 2;
+    const int rows = min(BM, t.g1 - t.i0);
+    const __amdgpu_buffer_rsrc_t h_rs =
+        make_rsrc(static_cast<uint16_t*>(p.out) + static_cast<long long>(t.i0) * p.N,
+                  static_cast<long long>(rows) * p.N * 2);
+    const __amdgpu_buffer_rsrc_t a_rs =
+        make_rsrc(static_cast<uint16_t*>(p.out2) + static_cast<long long>(t.i0) * F,
+                  static_cast<long long>(rows) * F * 2);
     const int f = j0 + wn * 32 + (lane & 31);
+    const int lrow = wm * WM + (lane >> 5) * 4;
+    const unsigned h_off = f < F ? static_cast<unsigned>((lrow * p.N + f) * 2) : kOOB;
+    const unsigned a_off = f < F ? static_cast<unsigned>((lrow * F + f) * 2) : kOOB;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int ra = t.i0 + wm * WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (ra < t.g1 && f < F) {
-          const uint16_t gb = f32_to_bf16(acc[i][0][r]), ub = f32_to_bf16(acc[i][1][r]);
-          uint16_t* hr = static_cast<uint16_t*>(p.out) + static_cast<long long>(ra) * p.N;
-          hr[f] = gb;
-          hr[F + f] = ub;
-          const float g = bf16_to_f32(gb), u = bf16_to_f32(ub);
-          static_cast<uint16_t*>(p.out2)[static_cast<long long>(ra) * F + f] =
-              f32_to_bf16(g * (1.f / (1.f + expf(-g))) * u);
-        }
+        const int row_c = i * 32 + (r >> 2) * 8 + (r & 3);
+        const unsigned ho = h_off + static_cast<unsigned>(row_c * p.N * 2);
+        const unsigned ao = a_off + static_cast<unsigned>(row_c * F * 2);
+        const uint16_t gb = f32_to_bf16(acc[i][0][r]), ub = f32_to_bf16(acc[i][1][r]);
+        __builtin_amdgcn_raw_buffer_store_b16(gb, h_rs, ho, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(ub, h_rs, ho + static_cast<unsigned>(F * 2), 0, 0);
+        const float g = bf16_to_f32(gb), u = bf16_to_f32(ub);
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(g * sigmoid_fast(g) * u), a_rs, ao, 0,
+                                              0);
       }
     }
     return;

@@ -60,6 +60,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// ---------------------------------------------------------------- math
+// sigmoid(z) = 1 / (1 + e^-z) from the hardware exp2 and reciprocal
+// (v_exp_f32, v_rcp_f32; about 1 ulp each).  Saturates to 0 / 1 for large
+// |z|.  Every kernel that evaluates SwiGLU uses this one, so fused and
+// separate evaluations agree bit for bit.
+__device__ __forceinline__ float sigmoid_fast(float z) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+}
+
 // ---------------------------------------------------------------- wave ops
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
