@@ -493,13 +493,30 @@ __device__ __forceinline__ void issue_step(const XL& xl, const YL& yl, const Buf
   if constexpr (YS) yl.issue(yb.b[s & 3], t);
 }
 
+// Scheduling pattern for a half step: each MFMA followed by up to two LDS
+// fragment reads and one global load.  The next half's fragments are then
+// all requested within the first MFMAs and have the rest of the half to
+// arrive, and the eight waves spread their LDS reads over the half instead of
+// all reading in one burst.  (Left to itself the compiler sinks each read to
+// just before its use and the MFMAs wait on LDS latency.)
+template <int NM>
+__device__ __forceinline__ void interleave_mfma_ds() {
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+  }
+}
+
 // The reduction loop of one workgroup tile.  Every wave issues its share of
 // the loads and takes part in every barrier; only the MFMAs (and fragment
 // reads) of row blocks past the end of the group are left out.
 //
-// Step s:  read k-slice 1 of step s | MFMAs on slice 0 | wait for this wave's
-// reads and for the loads step s + 1 needs, barrier | issue the loads of step
-// s + 4 | MFMAs on slice 1 | read slice 0 of step s + 1.  Loads go out in
+// Step s:  read k-slice 1 of step s, interleaved with the MFMAs on slice 0 |
+// wait for this wave's reads and for the loads step s + 1 needs, barrier |
+// issue the loads of step s + 4 and read slice 0 of step s + 1, interleaved
+// with the MFMAs on slice 1.  Loads go out in
 // step order (a step's pair before its quads), so what step s + 1 needs --
 // its quads, issued with step s + 1, and when s + 1 is even its pair, issued
 // with step s + 2 -- has landed once no more than the loads of the later
@@ -524,6 +541,8 @@ __device__ __forceinline__ void reduce_tile(f32x16 (&acc)[MI][NI], const XL& xl,
     for (int s = 0; s < 4; ++s) {
       read_frags<MIV, XS, YS>(f1, xb, yb, s, 1, xa, ya);
       mfma_step<MIV>(acc, f0);
+      interleave_mfma_ds<MIV * NI>();
+      __builtin_amdgcn_sched_barrier(0);
       // Issued after the loads step s + 1 needs: steps s + 2 and s + 3, minus
       // the pair of step s + 2 when that is the pair step s + 1 needs.
       if ((s & 1) == 0)
@@ -532,8 +551,10 @@ __device__ __forceinline__ void reduce_tile(f32x16 (&acc)[MI][NI], const XL& xl,
         wait_vmcnt_lgkm0<2 * LQ>();
       __builtin_amdgcn_s_barrier();
       issue_step<XS, YS>(xl, yl, xb, yb, s, kt + s + 4);
-      mfma_step<MIV>(acc, f1);
       read_frags<MIV, XS, YS>(f0, xb, yb, s + 1, 0, xa, ya);
+      mfma_step<MIV>(acc, f1);
+      interleave_mfma_ds<MIV * NI>();
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   // Drain the loads of the last steps before the workgroup's LDS is released.
