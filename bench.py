@@ -298,33 +298,71 @@ def main():
     bias = None if inp.bias is None else torch.from_numpy(inp.bias).to(dev)
     forced = None if inp.forced_idx is None else torch.from_numpy(inp.forced_idx).to(dev)
     layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, dtype=tdt, device=dev)
+    work = call_work(wl, b)
 
     def step():
         layer.forward(x, wr, w1, w2, bias=bias, forced_idx=forced)
         layer.backward(dy)
 
+    class Recorder:
+        """Event spans around the layer's calls (all of them, or only `names`)."""
+
+        def __init__(self, names=None):
+            self.names = names
+            self.events = []  # (name, start_event, end_event)
+            rec = self
+
+            class Span:
+                def __init__(self, name):
+                    self.name = name
+                    self.on = rec.names is None or name in rec.names
+
+                def __enter__(self):
+                    if self.on:
+                        self.s = torch.cuda.Event(enable_timing=True)
+                        self.s.record()
+
+                def __exit__(self, *exc):
+                    if self.on:
+                        e = torch.cuda.Event(enable_timing=True)
+                        e.record()
+                        rec.events.append((self.name, self.s, e))
+
+            self.span = Span
+
+        def per_call_ms(self):
+            per = {}
+            for name, s0, e in self.events:
+                per.setdefault(name, []).append(s0.elapsed_time(e))
+            return {n: sum(v) / len(v) for n, v in per.items()}
+
+    # Warm-up, with every call timed: the per-call times pick the dominant
+    # kernel, the only one whose calls carry events in the timed region (an
+    # event pair costs the stream a few microseconds; ~40 of them per step
+    # would inflate the step time by ~4%).
     log(f"[bench] warmup {args.warmup}")
+    warm = Recorder()
+    layer.timer = warm.span
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    layer.timer = None
+    if not warm.events:  # --warmup 0: one untimed step to find the dominant kernel
+        layer.timer = warm.span
+        step()
+        torch.cuda.synchronize()
+        layer.timer = None
+    warm_ms = warm.per_call_ms()
+    kname = {n: kernel_name(L, n, wl, code) for n in GEMM_CALLS if n in warm_ms}
+    by_kernel = {}
+    for n, kn in kname.items():
+        by_kernel.setdefault(kn, []).append(n)
+    dom = max(by_kernel, key=lambda kn: sum(warm_ms[n] for n in by_kernel[kn]))
+    dom_calls = by_kernel[dom]
 
-    events = []  # (name, start_event, end_event)
-
-    class Span:
-        def __init__(self, name):
-            self.name = name
-
-        def __enter__(self):
-            self.s = torch.cuda.Event(enable_timing=True)
-            self.s.record()
-
-        def __exit__(self, *exc):
-            e = torch.cuda.Event(enable_timing=True)
-            e.record()
-            events.append((self.name, self.s, e))
-
-    layer.timer = Span
-    log(f"[bench] timing {args.steps} steps")
+    log(f"[bench] timing {args.steps} steps (events on {', '.join(dom_calls)})")
+    timed = Recorder(set(dom_calls))
+    layer.timer = timed.span
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -335,13 +373,27 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     tokens_per_s = wl.T / ((t1 - t0) / args.steps)
 
-    per_call = {}
-    for name, s, e in events:
-        per_call.setdefault(name, []).append(s.elapsed_time(e))
-    work = call_work(wl, b)
+    # Dominant kernel, from the events of the timed region.
+    dom_ms = timed.per_call_ms()
+    flops_per_launch = sum(work[n][0] for n in dom_calls) / len(dom_calls)
+    avg_launch_ms = sum(dom_ms[n] for n in dom_calls) / len(dom_calls)
+    achieved = flops_per_launch / (avg_launch_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": read_traffic(dom), "kernel": dom, "launches_per_step": len(dom_calls),
+                "flops_per_launch": flops_per_launch, "avg_launch_ms": round(avg_launch_ms, 4)}
+
+    # Per-call breakdown: a separate pass after the timed region, every call timed.
+    n_brk = min(args.steps, 10)
+    log(f"[bench] per-call breakdown over {n_brk} further steps")
+    brk = Recorder()
+    layer.timer = brk.span
+    for _ in range(n_brk):
+        step()
+    torch.cuda.synchronize()
+    layer.timer = None
     kernels = {}
-    for name, ts in per_call.items():
-        avg = sum(ts) / len(ts)
+    for name, avg in brk.per_call_ms().items():
         fl, by = work[name]
         rec = {"ms": round(avg, 4)}
         if fl:
@@ -358,25 +410,6 @@ def main():
     g_fl = sum(work[n][0] for n in EXPERT_GEMMS)
     g_ms = sum(kernels[n]["ms"] for n in EXPERT_GEMMS)
     gemm_frac = g_fl / (g_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
-
-    # Dominant kernel: the GEMM kernel instance with the largest time per step.
-    by_kernel = {}
-    for n in GEMM_CALLS:
-        if n not in kernels:  # (gemm1_fwd runs fused with the activation)
-            continue
-        kname = kernels[n]["kernel"]
-        agg = by_kernel.setdefault(kname, {"ms": 0.0, "flops": 0, "launches": 0})
-        agg["ms"] += kernels[n]["ms"]
-        agg["flops"] += work[n][0]
-        agg["launches"] += 1
-    dom, agg = max(by_kernel.items(), key=lambda kv: kv[1]["ms"])
-    flops_per_launch = agg["flops"] / agg["launches"]
-    avg_launch_ms = agg["ms"] / agg["launches"]
-    achieved = flops_per_launch / (avg_launch_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": read_traffic(dom), "kernel": dom, "launches_per_step": agg["launches"],
-                "flops_per_launch": flops_per_launch, "avg_launch_ms": round(avg_launch_ms, 4)}
 
     if args.copy_probe:
         n = 1 << 30
@@ -400,6 +433,7 @@ def main():
         "grouped_gemm_tflops": round(g_fl / (g_ms * 1e-3) / 1e12, 1),
         "roofline": roofline,
         "kernels": kernels,
+        "kernels_note": f"per-call times from {n_brk} steps after the timed region",
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: float64 oracle")
