@@ -14,7 +14,8 @@
 //               -> blk_cnt[e][b]                                  (workspace)
 //   2. scan:    one block: totals -> counts, offsets; per expert an exclusive
 //               scan over blocks -> blk_off[e][b] = first row of block b's
-//               slots of expert e
+//               slots of expert e.  Each expert gets a power-of-two group of
+//               threads (inside one wave) that each sum a run of blocks.
 //   3. scatter: block b re-reads its chunk; each wave ranks its slots with a
 //               64-lane match mask (one ballot per expert-id bit), adds the
 //               running per-(wave, expert) count and the block offset, and
@@ -26,7 +27,7 @@ namespace {
 
 constexpr int kCiBlock = 256;                 // 4 waves
 constexpr int kCiWaves = kCiBlock / kWave;
-constexpr int kCiChunk = 4096;                // slots per block
+constexpr int kCiChunk = 512;                 // slots per block (many blocks in flight)
 constexpr int kCiSub = kCiChunk / kCiWaves;   // slots per wave
 constexpr int kScanBlock = 1024;
 
@@ -51,43 +52,55 @@ __global__ __launch_bounds__(kScanBlock) void ci_scan_kernel(const int32_t* __re
                                                              int32_t* __restrict__ blk_off,
                                                              int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ offsets) {
-  __shared__ int32_t wave_tot[kScanBlock / kWave];
-  __shared__ int32_t carry_s;
+  __shared__ int32_t tot_s[MOE_MAX_EXPERTS];
+  __shared__ int32_t base_s[MOE_MAX_EXPERTS];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wid = threadIdx.x / kWave;
-  if (threadIdx.x == 0) carry_s = 0;
-  __syncthreads();
-  // E <= 1024 = block size: one expert per thread, processed in one pass.
-  for (int e0 = 0; e0 < E; e0 += kScanBlock) {
-    const int e = e0 + threadIdx.x;
-    int tot = 0;
-    if (e < E) {
-      const int32_t* row = blk_cnt + static_cast<size_t>(e) * nblk;
-      for (int b = 0; b < nblk; ++b) tot += row[b];
-    }
-    const int inc = wave_inclusive_scan(tot, lane);
-    if (lane == kWave - 1) wave_tot[wid] = inc;
-    __syncthreads();
-    int wprefix = 0;
-    for (int w = 0; w < wid; ++w) wprefix += wave_tot[w];
-    const int carry = carry_s;
-    const int excl = carry + wprefix + inc - tot;
-    if (e < E) {
-      counts[e] = tot;
-      offsets[e] = excl;
-      const int32_t* row = blk_cnt + static_cast<size_t>(e) * nblk;
-      int32_t* orow = blk_off + static_cast<size_t>(e) * nblk;
-      int run = excl;
-      for (int b = 0; b < nblk; ++b) {
-        orow[b] = run;
-        run += row[b];
-      }
-    }
-    __syncthreads();
-    if (threadIdx.x == kScanBlock - 1) carry_s = excl + tot;
-    __syncthreads();
+  // tpe threads per expert: a power of two with E * tpe <= kScanBlock (E <=
+  // 1024 = kScanBlock) and tpe <= 64, so an expert's threads share a wave.
+  int tpe = 1;
+  while (tpe < kWave && 2 * tpe * E <= kScanBlock) tpe *= 2;
+  const int per_t = (nblk + tpe - 1) / tpe;
+  const int e = threadIdx.x / tpe, sub = threadIdx.x % tpe;
+  const bool act = e < E;
+  const int b0 = min(nblk, sub * per_t), b1 = min(nblk, b0 + per_t);
+  const int32_t* row = blk_cnt + static_cast<size_t>(act ? e : 0) * nblk;
+  int part = 0;
+  if (act)
+    for (int b = b0; b < b1; ++b) part += row[b];
+  // Inclusive scan over the expert's tpe threads, then its total.
+  int inc = part;
+  for (int o = 1; o < tpe; o <<= 1) {
+    const int n = __shfl_up(inc, o, tpe);
+    if (sub >= o) inc += n;
   }
-  if (threadIdx.x == 0) offsets[E] = carry_s;
+  const int tot = __shfl(inc, tpe - 1, tpe);
+  if (act && sub == 0) tot_s[e] = tot;
+  __syncthreads();
+  // Exclusive scan of the totals over experts (wave 0).
+  if (threadIdx.x < kWave) {
+    int carry = 0;
+    for (int c = 0; c < E; c += kWave) {
+      const int v = c + lane < E ? tot_s[c + lane] : 0;
+      const int iv = wave_inclusive_scan(v, lane);
+      if (c + lane < E) base_s[c + lane] = carry + iv - v;
+      carry += __shfl(iv, kWave - 1, kWave);
+    }
+    if (lane == 0) offsets[E] = carry;
+  }
+  __syncthreads();
+  if (act) {
+    const int base = base_s[e];
+    if (sub == 0) {
+      counts[e] = tot;
+      offsets[e] = base;
+    }
+    int32_t* orow = blk_off + static_cast<size_t>(e) * nblk;
+    int run = base + inc - part;
+    for (int b = b0; b < b1; ++b) {
+      orow[b] = run;
+      run += row[b];
+    }
+  }
 }
 
 // Lanes of the wave whose id equals this lane's id (only among lanes with
