@@ -250,6 +250,8 @@ def main():
                     help="tokens of the CPU-oracle sample (default: the whole workload; "
                          "two passes take about 15 s on 16 host cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--overlap-wgrad", action="store_true",
+                    help="expert weight-gradient GEMMs on a second stream")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="write a text summary of a rocprofv3 --kernel-trace --stats output")
@@ -297,7 +299,8 @@ def main():
     x, wr, w1, w2, dy = up(inp.x), up(inp.wr), up(inp.w1), up(inp.w2), up(inp.dy)
     bias = None if inp.bias is None else torch.from_numpy(inp.bias).to(dev)
     forced = None if inp.forced_idx is None else torch.from_numpy(inp.forced_idx).to(dev)
-    layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, dtype=tdt, device=dev)
+    layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, dtype=tdt, device=dev,
+                     overlap_wgrad=args.overlap_wgrad)
     work = call_work(wl, b)
 
     def step():
@@ -428,7 +431,8 @@ def main():
         "config": {"workload": f"{wl.name}: MoE layer T={wl.T} d={wl.d} E={wl.E} top-{wl.k} "
                                f"SwiGLU d_ff={wl.F}, fwd+bwd",
                    "T": wl.T, "d_model": wl.d, "experts": wl.E, "top_k": wl.k, "d_ff": wl.F,
-                   "regime": wl.regime, "parallelism": "single GPU"},
+                   "regime": wl.regime, "parallelism": "single GPU",
+                   "streams": 2 if args.overlap_wgrad else 1},
         "grouped_gemm_frac_of_bf16_peak": round(gemm_frac, 4),
         "grouped_gemm_tflops": round(g_fl / (g_ms * 1e-3) / 1e12, 1),
         "roofline": roofline,

@@ -2,7 +2,7 @@
 
 Every arithmetic step runs in the HIP library; this module only owns the
 device buffers (allocated once through torch) and sequences the calls on one
-stream.  No host synchronisation happens inside a pass: the per-expert
+stream (two with ``overlap_wgrad``).  No host synchronisation happens inside a pass: the per-expert
 offsets produced by counting stay on the device and are read there by the
 grouped GEMMs.
 
@@ -50,13 +50,15 @@ class MoELayer:
     """Buffers and call sequence for a fixed shape (T, d, E, k, F, dtype).
 
     ``dtype`` is ``torch.bfloat16`` (fp32 accumulation inside the kernels) or
-    ``torch.float32``.  Inputs are passed to :meth:`forward`; the returned
+    ``torch.float32``.  ``overlap_wgrad`` runs the two expert weight-gradient
+    GEMMs on a second stream, beside the data-gradient chain; the results are
+    the same bits either way.  Inputs are passed to :meth:`forward`; the returned
     tensors are views of buffers owned by the layer and are overwritten by the
     next call.
     """
 
     def __init__(self, T, d, E, k, F, dtype=torch.bfloat16, device="cuda", renorm=False,
-                 fuse_act=True):
+                 fuse_act=True, overlap_wgrad=False):
         if not (1 <= k <= E):
             raise ValueError("need 1 <= k <= E")
         self.T, self.d, self.E, self.k, self.F = T, d, E, k, F
@@ -64,6 +66,7 @@ class MoELayer:
         self.code = L.dtype_code(dtype)
         self.renorm = bool(renorm)
         self.fuse_act = bool(fuse_act)
+        self.overlap_wgrad = bool(overlap_wgrad)
         self.device = torch.device(device)
         Tk = T * k
         self.Tk = Tk
@@ -107,6 +110,15 @@ class MoELayer:
         self.gemm_ws_bytes = max(sizes)
         self.gemm_ws = (torch.empty(self.gemm_ws_bytes, dtype=torch.uint8, device=dev)
                         if self.gemm_ws_bytes else None)
+        # Expert weight gradients on a second stream (own workspace), joined
+        # at the end of backward.
+        if self.overlap_wgrad:
+            self.side = torch.cuda.Stream(device=dev)
+            self.gemm_ws2 = (torch.empty(self.gemm_ws_bytes, dtype=torch.uint8, device=dev)
+                             if self.gemm_ws_bytes else None)
+            self.ev_dyp = torch.cuda.Event()
+            self.ev_dh = torch.cuda.Event()
+            self.ev_side = torch.cuda.Event()
         self._inputs = None
         # Optional callable name -> context manager, wrapped around every
         # library call (used by the benchmark to bracket calls with events).
@@ -155,36 +167,56 @@ class MoELayer:
         T, d, E, k, F, Tk, c = self.T, self.d, self.E, self.k, self.F, self.Tk, self.code
         s = stream
         ws, wsb = self.gemm_ws, self.gemm_ws_bytes
+        overlap = self.overlap_wgrad and (s is None or isinstance(s, torch.cuda.Stream))
+        main = (s if s is not None else torch.cuda.current_stream(self.device)) if overlap else s
         with self._span("unpermute_bwd"):
             L.moe_unpermute_bwd(dy, self.yp, self.dest, self.w, T, k, d, c, self.dyp, self.dw,
-                                stream=s)
+                                stream=main)
+        if overlap:
+            self.ev_dyp.record(main)
         with self._span("gemm2_bwd_da"):
             L.moe_grouped_gemm_bwd(self.a, w2, self.dyp, self.offsets, Tk, F, d, E, c, self.da,
-                                   None, None, ws, wsb, stream=s)
-        # Each product is consumed right after it is made (da by the activation
-        # backward, dxp by the permutation backward), while it is still in the
-        # last-level cache; the weight gradients, which stream the most data,
-        # come after.
+                                   None, None, ws, wsb, stream=main)
         with self._span("act_bwd"):
-            L.moe_act_bwd(self.h, self.da, Tk, F, c, self.dh, stream=s)
-        with self._span("gemm2_bwd_dw"):
-            L.moe_grouped_gemm_bwd(self.a, w2, self.dyp, self.offsets, Tk, F, d, E, c, None,
-                                   None, self.dw2, ws, wsb, stream=s)
+            L.moe_act_bwd(self.h, self.da, Tk, F, c, self.dh, stream=main)
+        if overlap:
+            # Weight gradients on the side stream: dW2 once dyp exists, dW1
+            # once dh exists; they fill the compute units the data-gradient
+            # chain leaves idle (kernel tails, memory-bound kernels).
+            self.ev_dh.record(main)
+            side, ws2 = self.side, self.gemm_ws2
+            side.wait_event(self.ev_dyp)
+            with torch.cuda.stream(side):
+                with self._span("gemm2_bwd_dw"):
+                    L.moe_grouped_gemm_bwd(self.a, w2, self.dyp, self.offsets, Tk, F, d, E, c,
+                                           None, None, self.dw2, ws2, wsb, stream=side)
+                side.wait_event(self.ev_dh)
+                with self._span("gemm1_bwd_dw"):
+                    L.moe_grouped_gemm_bwd(self.xp, w1, self.dh, self.offsets, Tk, d, 2 * F, E,
+                                           c, None, None, self.dw1, ws2, wsb, stream=side)
+            self.ev_side.record(side)
+        else:
+            with self._span("gemm2_bwd_dw"):
+                L.moe_grouped_gemm_bwd(self.a, w2, self.dyp, self.offsets, Tk, F, d, E, c, None,
+                                       None, self.dw2, ws, wsb, stream=main)
         with self._span("gemm1_bwd_da"):
             L.moe_grouped_gemm_bwd(self.xp, w1, self.dh, self.offsets, Tk, d, 2 * F, E, c,
-                                   self.dxp, None, None, ws, wsb, stream=s)
+                                   self.dxp, None, None, ws, wsb, stream=main)
         with self._span("permute_bwd"):
-            L.moe_unpermute(self.dxp, self.dest, None, T, k, d, c, self.dx_e, stream=s)
-        with self._span("gemm1_bwd_dw"):
-            L.moe_grouped_gemm_bwd(self.xp, w1, self.dh, self.offsets, Tk, d, 2 * F, E, c, None,
-                                   None, self.dw1, ws, wsb, stream=s)
+            L.moe_unpermute(self.dxp, self.dest, None, T, k, d, c, self.dx_e, stream=main)
+        if not overlap:
+            with self._span("gemm1_bwd_dw"):
+                L.moe_grouped_gemm_bwd(self.xp, w1, self.dh, self.offsets, Tk, d, 2 * F, E, c,
+                                       None, None, self.dw1, ws, wsb, stream=main)
         with self._span("route_topk_bwd"):
             L.moe_route_topk_bwd(self.probs, self.idx, self.dw, T, E, k, self.renorm,
-                                 self.dlogits, c, stream=s)
+                                 self.dlogits, c, stream=main)
         with self._span("router_bwd_da"):
             L.moe_grouped_gemm_bwd(x, wr, self.dlogits, self.router_offsets, T, d, E, 1, c,
-                                   self.dx, self.dx_e, None, ws, wsb, stream=s)
+                                   self.dx, self.dx_e, None, ws, wsb, stream=main)
         with self._span("router_bwd_dw"):
             L.moe_grouped_gemm_bwd(x, wr, self.dlogits, self.router_offsets, T, d, E, 1, c,
-                                   None, None, self.dwr, ws, wsb, stream=s)
+                                   None, None, self.dwr, ws, wsb, stream=main)
+        if overlap:
+            main.wait_event(self.ev_side)
         return Grads(self.dx, self.dwr, self.dw1, self.dw2)

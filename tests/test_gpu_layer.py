@@ -24,12 +24,12 @@ def _native_lib():
     import mixture_experts_layer_gating_amd._lib  # noqa: F401  (raises if not built)
 
 
-def _run(inp, renorm=False, fuse_act=True):
+def _run(inp, renorm=False, fuse_act=True, overlap_wgrad=False):
     from mixture_experts_layer_gating_amd.layer import MoELayer
     wl = inp.wl
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, dtype=tdt, device=DEV, renorm=renorm,
-                     fuse_act=fuse_act)
+                     fuse_act=fuse_act, overlap_wgrad=overlap_wgrad)
     x, wr, w1, w2, dy = (dev(a, tdt) for a in (inp.x, inp.wr, inp.w1, inp.w2, inp.dy))
     bias = None if inp.bias is None else dev(inp.bias)
     forced = None if inp.forced_idx is None else dev(inp.forced_idx)
@@ -175,3 +175,23 @@ def test_layer_fused_activation_matches_unfused():
     np.testing.assert_array_equal(ya, host(lb.y))
     for k, v in da.items():
         np.testing.assert_array_equal(v, host(getattr(gb, k)), err_msg=k)
+
+
+def test_layer_overlapped_weight_gradients_match():
+    """The weight-gradient GEMMs on a second stream give the same bits as the
+    one-stream sequence, over two steps in a row (the second step's forward
+    must not overwrite what the first step's side stream still reads)."""
+    wl = Workload("ovl", T=2048, d=512, E=16, k=4, F=256, dtype="bf16", w_std=0.05, seed=37,
+                  regime="skew")
+    say(f"layer overlapped weight gradients {wl}")
+    inp = make_inputs(wl)
+    la, ga, args = _run(inp, overlap_wgrad=False)
+    want = {k: host(getattr(ga, k)).copy() for k in ("dx", "dwr", "dw1", "dw2")}
+    lb, gb, _ = _run(inp, overlap_wgrad=True)
+    x, wr, w1, w2, dy, bias, forced = args
+    for _ in range(2):
+        for k, v in want.items():
+            np.testing.assert_array_equal(v, host(getattr(gb, k)), err_msg=k)
+        lb.forward(x, wr, w1, w2, bias=bias, forced_idx=forced)
+        gb = lb.backward(dy)
+        torch.cuda.synchronize()
