@@ -516,12 +516,12 @@ __device__ __forceinline__ void interleave_mfma_ds() {
 // Step s:  read k-slice 1 of step s, interleaved with the MFMAs on slice 0 |
 // wait for this wave's reads and for the loads step s + 1 needs, barrier |
 // issue the loads of step s + 4 and read slice 0 of step s + 1, interleaved
-// with the MFMAs on slice 1.  Loads go out in
-// step order (a step's pair before its quads), so what step s + 1 needs --
-// its quads, issued with step s + 1, and when s + 1 is even its pair, issued
-// with step s + 2 -- has landed once no more than the loads of the later
-// steps up to s + 3 are outstanding.  Steps past the reduction range load
-// zeros; the loop runs a multiple of 4 steps.
+// with the MFMAs on slice 1.  Loads go out in step order (a step's pair
+// before its quads), so what step s + 1 needs -- its quads, issued with step
+// s + 1, and when s + 1 is even its pair, issued with step s + 2 -- has
+// landed once no more than the loads of the later steps up to s + 3 are
+// outstanding.  Steps past the reduction range load zeros; the loop runs a
+// multiple of 4 steps.
 template <int MIV, bool XS, bool YS, int MI, int NI, class XL, class YL, class XA, class YA>
 __device__ __forceinline__ void reduce_tile(f32x16 (&acc)[MI][NI], const XL& xl, const YL& yl,
                                             const XA& xa, const YA& ya, const Bufs& xb,
