@@ -240,6 +240,7 @@ __device__ bool resolve_tile(const GemmArgs& p, int* sh, TileInfo& t) {
 constexpr int kBK = 32;
 constexpr int kThreads = 256;           // SIMT fallback: 256 threads per block
 constexpr unsigned kOOB = 0x80000000u;  // buffer offset that is always out of range
+constexpr int kCpolNonTemporal = 2;     // cache-policy operand of buffer stores: nt
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -720,6 +721,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
   // store needs a branch.
   {
     constexpr int SZ = sizeof(OutT);
+    // Weight gradients are not read again in the pass: non-temporal stores
+    // keep them from displacing the activations that the next kernels read
+    // from the caches (full layer -0.7%).  Other results are read by the
+    // next kernel and keep the default policy.
+    constexpr int kOutCpol = MODE == kTN ? kCpolNonTemporal : 0;
     const int ld = (MODE == kNT) ? p.K : p.N;  // output row length
     const int row_end = (MODE == kTN) ? p.K : t.g1;
     const int rows = min(BM, row_end - t.i0);
@@ -775,7 +781,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
             if constexpr (SZ == 2)
               __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), out_rs, off, 0, 0);
             else
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), out_rs, off, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), out_rs, off, 0, kOutCpol);
           }
         }
       }
