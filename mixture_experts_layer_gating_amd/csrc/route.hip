@@ -9,7 +9,11 @@
 //
 // Layout: one 64-lane wavefront per token, expert e held by lane e % 64 in
 // register slot e / 64.  Selection is k rounds of a wave-wide (value, index)
-// arg-max; nothing is written to global memory but the outputs.
+// arg-max; nothing is written to global memory but the outputs.  With at
+// most 64 experts a token takes 8 lanes instead (8 tokens per wavefront,
+// lane g of a group holding experts g*V .. g*V + V - 1, V = ceil(E / 8)):
+// the same k rounds, each a scan of V registers and a 3-step arg-max across
+// the group, at an eighth of the wavefronts.
 #include <float.h>
 #include <math.h>
 
@@ -122,6 +126,139 @@ __global__ __launch_bounds__(kRouteBlock) void route_topk_kernel(
   }
 }
 
+// At most 64 experts: 8 lanes per token (see the layout note above).  Same
+// definitions as route_topk_kernel; the softmax sum is taken in a different
+// order (per lane, then across the 8 lanes).
+constexpr int kGroup = 8;  // lanes per token
+
+template <int V>
+__global__ __launch_bounds__(kRouteBlock) void route_topk_small_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int T, int E,
+    int k, int renorm, const int32_t* __restrict__ forced, int32_t* __restrict__ idx_out,
+    float* __restrict__ w_out, float* __restrict__ probs) {
+  constexpr int kSlots = MOE_MAX_TOPK / kGroup;  // output slots per lane
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g = lane & (kGroup - 1);
+  const int t = blockIdx.x * (kRouteBlock / kGroup) + static_cast<int>(threadIdx.x / kGroup);
+  // Whole groups leave together (all 8 lanes share t), so the shuffles below
+  // only ever read lanes of live groups.
+  if (t >= T) return;
+  const float* row = logits + static_cast<size_t>(t) * E;
+
+  float z[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int e = g * V + v;
+    if (e < E) {
+      float x = row[e];
+      if (bias) x = x + bias[e];
+      z[v] = x;
+    } else {
+      z[v] = -INFINITY;
+    }
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < V; ++v) m = fmaxf(m, z[v]);
+#pragma unroll
+  for (int o = kGroup / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+  float ex[V];
+  float s = 0.f;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    ex[v] = (g * V + v < E) ? expf(z[v] - m) : 0.f;
+    s += ex[v];
+  }
+#pragma unroll
+  for (int o = kGroup / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
+  if (probs) {
+    float* prow = probs + static_cast<size_t>(t) * E;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (g * V + v < E) prow[g * V + v] = ex[v] / s;
+  }
+
+  // Slot j goes to lane j % 8 of the group, register j / 8.
+  int my_id[kSlots];
+  float my_p[kSlots];
+#pragma unroll
+  for (int q = 0; q < kSlots; ++q) {
+    my_id[q] = 0;
+    my_p[q] = 0.f;
+  }
+  if (forced) {
+#pragma unroll
+    for (int q = 0; q < kSlots; ++q) {
+      const int j = q * kGroup + g;
+      if (j < k) {
+        const int e = forced[static_cast<size_t>(t) * k + j];
+        float x = row[e];
+        if (bias) x = x + bias[e];
+        my_id[q] = e;
+        my_p[q] = expf(x - m) / s;
+      }
+    }
+  } else {
+    uint32_t taken = 0;  // bit v: register v already selected
+    for (int j = 0; j < k; ++j) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int e = g * V + v;
+        if (e < E && !(taken & (1u << v)) && better(z[v], e, bv, bi)) {
+          bv = z[v];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int o = kGroup / 2; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, kWave);
+        const int oi = __shfl_xor(bi, o, kWave);
+        if (better(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      // Every lane of the group now holds the winner (bv, bi).
+      if (bi / V == g) taken |= 1u << (bi - g * V);
+      if ((j & (kGroup - 1)) == g) {
+        const float p = expf(bv - m) / s;
+#pragma unroll
+        for (int q = 0; q < kSlots; ++q)
+          if (q == j / kGroup) {
+            my_id[q] = bi;
+            my_p[q] = p;
+          }
+      }
+    }
+  }
+  if (renorm) {
+    // Sum over j in increasing order, identical in every lane of the group.
+    const int base = lane & ~(kGroup - 1);
+    float tot = 0.f;
+    for (int j = 0; j < k; ++j) {
+      float pj = 0.f;
+#pragma unroll
+      for (int q = 0; q < kSlots; ++q) {
+        const float x = __shfl(my_p[q], base + (j & (kGroup - 1)), kWave);
+        if (q == j / kGroup) pj = x;
+      }
+      tot += pj;
+    }
+#pragma unroll
+    for (int q = 0; q < kSlots; ++q) my_p[q] = my_p[q] / tot;
+  }
+#pragma unroll
+  for (int q = 0; q < kSlots; ++q) {
+    const int j = q * kGroup + g;
+    if (j < k) {
+      idx_out[static_cast<size_t>(t) * k + j] = my_id[q];
+      w_out[static_cast<size_t>(t) * k + j] = my_p[q];
+    }
+  }
+}
+
 template <int EPL, typename OutT>
 __global__ __launch_bounds__(kRouteBlock) void route_topk_bwd_kernel(
     const float* __restrict__ probs, const int32_t* __restrict__ idx,
@@ -217,8 +354,22 @@ extern "C" moe_status moe_route_topk(const float* logits, const float* bias, int
   if (moe_status st = check_route_sizes(T, E, k)) return st;
   MOE_REQUIRE(logits && topk_idx && topk_w, MOE_ERR_INVALID_ARG,
               "moe_route_topk: null logits/topk_idx/topk_w");
-  const dim3 grid((T + 3) / 4);
   hipStream_t st = as_stream(stream);
+  if (E <= kWave) {
+    // 8 lanes per token, 32 tokens per block
+    const dim3 g8((T + kRouteBlock / kGroup - 1) / (kRouteBlock / kGroup));
+    const int v = (E + kGroup - 1) / kGroup;
+#define MOE_SMALL(VV)                                                                         \
+  hipLaunchKernelGGL(route_topk_small_kernel<VV>, g8, dim3(kRouteBlock), 0, st, logits, bias, T, \
+                     E, k, renorm, forced_idx, topk_idx, topk_w, probs)
+    if (v <= 1) MOE_SMALL(1);
+    else if (v <= 2) MOE_SMALL(2);
+    else if (v <= 4) MOE_SMALL(4);
+    else MOE_SMALL(8);
+#undef MOE_SMALL
+    return check_launch("moe_route_topk");
+  }
+  const dim3 grid((T + 3) / 4);
   const int epl = (E + kWave - 1) / kWave;
   if (epl <= 1)
     launch_route<1>(T, grid, st, logits, bias, E, k, renorm, forced_idx, topk_idx, topk_w, probs);

@@ -40,8 +40,11 @@ def _run_route(logits, k, bias=None, forced=None, renorm=False):
     return host(idx), host(w), host(p)
 
 
+# E <= 64 runs the 8-lanes-per-token kernel (experts per lane V = 1, 2, 4, 8;
+# k > 8 puts several slots in a lane), larger E the one-wave-per-token kernel.
 ROUTE_CASES = [(1, 1, 1), (7, 3, 2), (513, 8, 2), (8192, 64, 8), (300, 65, 8), (128, 128, 8),
-               (512, 256, 8), (64, 1024, 32), (100, 200, 1), (33, 16, 16)]
+               (512, 256, 8), (64, 1024, 32), (100, 200, 1), (33, 16, 16), (257, 32, 32),
+               (99, 40, 24), (70, 64, 9)]
 
 
 @pytest.mark.parametrize("T,E,k", ROUTE_CASES)
@@ -57,9 +60,10 @@ def test_route_topk(T, E, k, ties):
 
 
 @pytest.mark.parametrize("renorm", [False, True])
-def test_route_bias_forced_renorm(renorm):
-    T, E, k = 2048, 64, 8
-    say(f"route_topk bias/forced renorm={renorm}")
+@pytest.mark.parametrize("E", [64, 96])
+def test_route_bias_forced_renorm(renorm, E):
+    T, k = 2048, 8
+    say(f"route_topk bias/forced renorm={renorm} E={E}")
     logits = _logits(T, E, 5, False)
     bias = (-1.2 * np.log(np.random.default_rng(6).permutation(E) + 1.0)).astype(np.float32)
     idx, w, p = _run_route(logits, k, bias=bias, renorm=renorm)
