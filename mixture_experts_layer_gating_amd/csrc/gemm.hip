@@ -12,19 +12,28 @@
 //   NT  da[rows e] = dc[rows e] @ b[e]^T        input gradient (over N)
 //   TN  db[e]      = a[rows e]^T @ dc[rows e]   weight gradient (over rows)
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16 (gfx950) on BMxBNx64 tiles, 4 waves in
-// a 2x2 grid, each wave (BM/2)x(BN/2).  Operand tiles are staged through LDS
-// in a k-contiguous layout, double-buffered (global loads of step k+1 are in
-// flight while the MFMAs of step k run), with the 16-byte chunk index XORed
-// with (row % 8) so that both the LDS writes and the MFMA fragment reads are
-// bank-conflict free.  An operand whose reduction index is not contiguous in
-// memory (b in NN; a and dc in TN) is loaded as 8x8 blocks and transposed in
-// registers before the LDS write.  Workgroup ids are remapped so that each
-// of the 8 XCDs (own L2) walks a contiguous range of tiles, which keeps one
-// expert's weights and rows in one L2.
+// bf16 path (gemm_mfma_kernel): v_mfma_f32_32x32x16_bf16 on tiles of up to
+// 256x256 outputs, 8 waves (2x4, 128x64 per wave, two per SIMD) for the big
+// tiles; smaller tiles for small shapes.  Operands go from global memory
+// straight into LDS (buffer_load ... lds, one 1 KB wave instruction at a
+// time), four reduction steps of 32 in flight:
+//   * k-contiguous operands (a in NN, both in NT) in two "pair" buffers of
+//     [rows][64] (two steps each; whole 128-byte lines per request), read
+//     with ds_read_b128 through an XOR swizzle of the 16-byte chunk;
+//   * k-strided operands (b in NN, both in TN) in four "quad" buffers of
+//     [32][cols], read with gfx950's transposing ds_read_b64_tr_b16.
+// Waits are counted vmcnt waits plus one barrier per step; the MFMAs are
+// interleaved with the next half-step's fragment reads and loads.  The
+// epilogue converts and stores through buffer descriptors over the tile's
+// valid rows (GEMM 1 can apply SwiGLU there).  Workgroups are mapped so that
+// each of the 8 XCDs (own L2) walks a contiguous range of tiles, which keeps
+// one expert's weights and rows in one L2; weight-gradient tile rows are
+// dealt over the XCDs in pairs (balance under skewed routing).  Shapes with
+// few output tiles reduce the weight gradient in row slices (partials in a
+// workspace, summed in slice order).
 //
 // Float32 (and shapes whose K or N is not a multiple of 8) run on a plain
-// LDS-tiled FMA kernel with the same tile resolution.
+// LDS-tiled FMA kernel (gemm_simt_kernel) with the same tile resolution.
 #include <math.h>
 
 #include <type_traits>
