@@ -86,7 +86,10 @@ EXPERT_GEMMS = ("gemm1_swiglu_fwd", "gemm2_fwd", "gemm2_bwd_da", "gemm2_bwd_dw",
                 "gemm1_bwd_da", "gemm1_bwd_dw")
 
 
-def kernel_name(L, call, wl, code):
+GATHER_CALLS = ("gemm1_swiglu_fwd", "gemm1_bwd_dw")  # read x through src / k when gathering
+
+
+def kernel_name(L, call, wl, code, gather=False):
     """Name (as rocprofv3 prints it) of the kernel a GEMM call launches."""
     prod, M, K, N, E = GEMM_CALLS[call](wl)
     plan = L.moe_grouped_gemm_plan(prod, M, K, N, E, code)
@@ -95,8 +98,9 @@ def kernel_name(L, call, wl, code):
     out = "float" if prod == 2 or call == "router_fwd" else "unsigned short"
     mode = 0 if prod == 3 else prod
     glu = "true" if prod == 3 else "false"
+    gx = "true" if gather and call in GATHER_CALLS else "false"
     return (f"gemm_mfma_kernel<{mode}, {plan['tile_m']}, {plan['tile_n']}, "
-            f"{plan['waves_m']}, {plan['waves_n']}, {out}, {glu}>")
+            f"{plan['waves_m']}, {plan['waves_n']}, {out}, {glu}, {gx}>")
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -356,7 +360,7 @@ def main():
         torch.cuda.synchronize()
         layer.timer = None
     warm_ms = warm.per_call_ms()
-    kname = {n: kernel_name(L, n, wl, code) for n in GEMM_CALLS if n in warm_ms}
+    kname = {n: kernel_name(L, n, wl, code, layer.gather_x) for n in GEMM_CALLS if n in warm_ms}
     by_kernel = {}
     for n, kn in kname.items():
         by_kernel.setdefault(kn, []).append(n)
@@ -406,7 +410,7 @@ def main():
             rec["gbs"] = round(by / (avg * 1e-3) / 1e9, 1)
             rec["frac_hbm"] = round(by / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
         if name in GEMM_CALLS:
-            rec["kernel"] = kernel_name(L, name, wl, code)
+            rec["kernel"] = kernel_name(L, name, wl, code, layer.gather_x)
         kernels[name] = rec
 
     # Grouped-GEMM share of the bf16 peak, over the six expert GEMM launches.

@@ -248,6 +248,39 @@ moe_status moe_grouped_gemm_swiglu_fwd(const void* a, const void* b,
                                        void* act, moe_stream_t stream);
 
 /*
+ * Gathered-operand variants: the permutation fused into the operand loads
+ * of the GEMMs that read the permuted activations [Brief, Core method: the
+ * index generation feeds the grouped GEMM].  Instead of a permuted copy
+ * a [M, K], they take the unpermuted array x [x_phys, K] and a row map:
+ * logical row p of a is row x_rows[p] / x_div of x.  With the outputs of
+ * moe_count_index, x_rows = src and x_div = k give a = xp without writing
+ * it (xp[p] = x[src[p] / k]).  Results equal, bit for bit, the plain call on
+ * the permuted copy.
+ *
+ * moe_grouped_gemm_swiglu_fwd_gather: moe_grouped_gemm_swiglu_fwd with a
+ *   gathered.
+ * moe_grouped_gemm_bwd_gather: moe_grouped_gemm_bwd with a gathered (only db
+ *   reads a).
+ *   x_rows int32 [M] device; every x_rows[p] / x_div (for the rows the
+ *   groups cover) must lie in [0, x_phys).  Requires the bf16 MFMA path
+ *   (K and F, or K and N, multiples of 8) and x_phys * K < 2^30;
+ *   MOE_ERR_UNSUPPORTED otherwise.  Other arguments, alignment, workspace
+ *   and errors as in the plain calls.
+ */
+moe_status moe_grouped_gemm_swiglu_fwd_gather(const void* x, const int32_t* x_rows,
+                                              int x_div, int x_phys, const void* b,
+                                              const int32_t* offsets, int M, int K,
+                                              int F, int E, moe_dtype dtype, void* h,
+                                              void* act, moe_stream_t stream);
+moe_status moe_grouped_gemm_bwd_gather(const void* a, const int32_t* a_rows,
+                                       int a_div, int a_phys, const void* b,
+                                       const void* dc, const int32_t* offsets,
+                                       int M, int K, int N, int E, moe_dtype dtype,
+                                       void* da, const void* da_add, float* db,
+                                       void* ws, size_t ws_bytes,
+                                       moe_stream_t stream);
+
+/*
  * moe_act_fwd -- SwiGLU activation [Summary, Method details / key design:
  * optimised activation]: a[m, f] = silu(h[m, f]) * h[m, F + f],
  * silu(z) = z / (1 + exp(-z)).   h [M, 2F], a [M, F], both `dtype`.

@@ -35,6 +35,7 @@ SYMBOLS = (
     "moe_unpermute", "moe_unpermute_bwd", "moe_grouped_gemm_workspace_size",
     "moe_grouped_gemm_plan",
     "moe_grouped_gemm_fwd", "moe_grouped_gemm_bwd", "moe_grouped_gemm_swiglu_fwd",
+    "moe_grouped_gemm_swiglu_fwd_gather", "moe_grouped_gemm_bwd_gather",
     "moe_act_fwd", "moe_act_bwd",
 )
 
@@ -96,6 +97,10 @@ _SIG = {
     "moe_grouped_gemm_fwd": ([_p, _p, _p, _i, _i, _i, _i, _i, _p, _i, _p, _z, _p], _i),
     "moe_grouped_gemm_bwd": ([_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _z, _p], _i),
     "moe_grouped_gemm_swiglu_fwd": ([_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p], _i),
+    "moe_grouped_gemm_swiglu_fwd_gather": ([_p, _p, _i, _i, _p, _p, _i, _i, _i, _i, _i, _p, _p,
+                                            _p], _i),
+    "moe_grouped_gemm_bwd_gather": ([_p, _p, _i, _i, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p,
+                                     _p, _z, _p], _i),
     "moe_act_fwd": ([_p, _i, _i, _i, _p, _p], _i),
     "moe_act_bwd": ([_p, _p, _i, _i, _i, _p, _p], _i),
 }
@@ -222,6 +227,20 @@ def moe_grouped_gemm_bwd(a, b, dc, offsets, M, K, N, E, dtype, da, da_add, db, w
 def moe_grouped_gemm_swiglu_fwd(a, b, offsets, M, K, F, E, dtype, h, act, stream=None):
     _check(_lib.moe_grouped_gemm_swiglu_fwd(_ptr(a), _ptr(b), _ptr(offsets), M, K, F, E, dtype,
                                             _ptr(h), _ptr(act), _stream(stream, a)))
+
+
+def moe_grouped_gemm_swiglu_fwd_gather(x, x_rows, x_div, x_phys, b, offsets, M, K, F, E, dtype,
+                                       h, act, stream=None):
+    _check(_lib.moe_grouped_gemm_swiglu_fwd_gather(
+        _ptr(x), _ptr(x_rows), x_div, x_phys, _ptr(b), _ptr(offsets), M, K, F, E, dtype, _ptr(h),
+        _ptr(act), _stream(stream, x)))
+
+
+def moe_grouped_gemm_bwd_gather(a, a_rows, a_div, a_phys, b, dc, offsets, M, K, N, E, dtype, da,
+                                da_add, db, ws=None, ws_bytes=0, stream=None):
+    _check(_lib.moe_grouped_gemm_bwd_gather(
+        _ptr(a), _ptr(a_rows), a_div, a_phys, _ptr(b), _ptr(dc), _ptr(offsets), M, K, N, E, dtype,
+        _ptr(da), _ptr(da_add), _ptr(db), _ptr(ws), ws_bytes, _stream(stream, dc)))
 
 
 def moe_act_fwd(h, M, F, dtype, a, stream=None):

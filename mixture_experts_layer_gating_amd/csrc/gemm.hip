@@ -60,6 +60,14 @@ struct GemmArgs {
   int ntn;    // column tiles
   int split;  // TN: reduction slices (partials written to out as [split][E][K][N])
   void* out2;  // NN with the SwiGLU epilogue: act [M, N / 2]
+  // Gathered x operand (GEMM 1 and its weight gradient without a permuted
+  // copy of x): logical row p of x is physical row xrows[p] / xdiv of the
+  // x array, which has xphys rows.  xrows == nullptr: x is used as is.
+  const int32_t* xrows;
+  int xdiv;
+  int xphys;
+  unsigned xmagic;  // ceil(2^32 / xdiv) mod 2^32 (see div_rows)
+  int xshift;       // log2(xdiv) when xdiv is a power of two, else -1
 };
 
 // ------------------------------------------------------------------ tiles
@@ -309,17 +317,42 @@ struct Operand {
   // i.e. memory column (o / 32 % 2) * glu_f + glu_j0 + f.  glu_f = 0: plain.
   int glu_f;
   int glu_j0;
+  // Gathered rows (loaders with GX): logical row p (k-contiguous: tile row;
+  // k-strided: reduction row) is physical row rows[p] / rdiv of base, which
+  // has `phys` rows; col0 is added to every column (k-strided).
+  const int32_t* rows;
+  int rdiv;
+  int phys;
+  int col0;
+  unsigned rmagic;  // ceil(2^32 / rdiv) mod 2^32
+  int rshift;       // log2(rdiv) when rdiv is a power of two, else -1
 };
+
+// n / d for 0 <= n < 2^31, 1 <= d, with m = ceil(2^32 / d) mod 2^32: the
+// high half of n * m is n / d or n / d + 1 (the excess of m over 2^32 / d
+// adds less than n / 2^32 < 1/2), one correction each way makes it exact;
+// d = 1 (m wraps to 0) is passed through.  A handful of instructions instead
+// of a full 32-bit division.
+__device__ __forceinline__ int div_rows(int n, int d, unsigned m) {
+  const unsigned un = static_cast<unsigned>(n), ud = static_cast<unsigned>(d);
+  unsigned q = __umulhi(un, m);
+  q -= (q * ud > un) ? 1u : 0u;
+  q += ((q + 1u) * ud <= un) ? 1u : 0u;
+  return d == 1 ? n : static_cast<int>(q);
+}
 
 // Loads of one operand, shared by the NW waves of the workgroup.  A k-strided
 // operand loads one reduction step (O x 32 elements, O / 16 wave
 // instructions) per call; a k-contiguous one loads a pair of steps (O x 64
 // elements, O / 8 wave instructions).
-template <bool STRIDED, int O, int NW>
+template <bool STRIDED, int O, int NW, bool GX = false>
 struct DmaLoader {
   static constexpr int kSpan = STRIDED ? kBK : 2 * kBK;  // reduction elements per call
   static constexpr int kTotal = O * kSpan * 2 / 1024;     // 1 KB wave instructions per call
   static constexpr int kPerWave = kTotal >= NW ? kTotal / NW : 1;
+  // Vector-memory loads per call and wave: the LDS loads, plus (gathered
+  // k-strided operand) the row-map loads of the call four ahead.
+  static constexpr int kLoadsPerCall = kPerWave * ((GX && STRIDED) ? 2 : 1);
   static_assert(kTotal % NW == 0 || kTotal < NW, "chunks must split evenly over waves");
   static_assert(NW % 2 == 0, "pair chunk mapping assumes an even number of waves");
   __amdgpu_buffer_rsrc_t rsrc;
@@ -327,6 +360,15 @@ struct DmaLoader {
   int lds_off[kPerWave];    // element offset in the buffer (wave-uniform)
   int klim;                 // k-contiguous: this lane's chunk loaded for call indices < klim
   unsigned step;            // bytes per call index
+  // Gathered k-strided operand: this lane's row within a call (per q), the
+  // tile's reduction range, the row map, and a ring of the physical rows of
+  // the next four calls (slot = call index % 4).
+  int grow[GX && STRIDED ? kPerWave : 1];
+  int g_lo, g_hi, g_div, g_shift;
+  unsigned g_magic;
+  unsigned ld_bytes;
+  __amdgpu_buffer_rsrc_t g_rs;  // the row map
+  int ring[GX && STRIDED ? kPerWave : 1][4];
 
   __device__ __forceinline__ void init(const Operand& op, int r_lo, int r_hi) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -346,7 +388,9 @@ struct DmaLoader {
         // while r_lo + i * 64 + c * 8 + 8 <= r_hi.
         const int room = r_hi - r_lo - c * 8 - 8;
         klim = room >= 0 ? room / kSpan + 1 : 0;
-        voff[q] = row < op.o_valid ? static_cast<unsigned>((row * op.ld + c * 8) * 2) : kOOB;
+        int prow = row;  // physical row
+        if constexpr (GX) prow = row < op.o_valid ? div_rows(op.rows[row], op.rdiv, op.rmagic) : 0;
+        voff[q] = row < op.o_valid ? static_cast<unsigned>((prow * op.ld + c * 8) * 2) : kOOB;
       } else {
         // Rows past the reduction range fall outside the buffer range; so do
         // columns past the operand (kOOB + i * step stays above the range,
@@ -362,10 +406,32 @@ struct DmaLoader {
         } else {
           valid = col + 8 <= op.o_valid;
         }
-        voff[q] = valid ? static_cast<unsigned>((row * op.ld + col) * 2) : kOOB;
+        if constexpr (GX) {
+          // row is this lane's row within a call; the physical row comes
+          // from the ring at issue time.
+          grow[q] = row;
+          voff[q] = valid ? static_cast<unsigned>((op.col0 + col) * 2) : kOOB;
+        } else {
+          voff[q] = valid ? static_cast<unsigned>((row * op.ld + col) * 2) : kOOB;
+        }
       }
     }
-    if constexpr (!STRIDED) {
+    if constexpr (GX) {
+      rsrc = make_rsrc(op.base, static_cast<long long>(op.phys) * op.ld * 2);
+      step = STRIDED ? 0u : static_cast<unsigned>(kSpan * 2);
+      if constexpr (STRIDED) {
+        g_lo = r_lo;
+        g_hi = r_hi;
+        g_magic = op.rmagic;
+        g_shift = op.rshift;
+        ld_bytes = static_cast<unsigned>(op.ld * 2);
+        g_div = op.rdiv;
+        g_rs = make_rsrc(op.rows, static_cast<long long>(r_hi > 0 ? r_hi : 1) * 4);
+        // Row maps of calls 0..3; the prologue's issues fetch those of 4..7.
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) fetch_rows(sl, sl);
+      }
+    } else if constexpr (!STRIDED) {
       const int rows = op.o_valid < O ? (op.o_valid < 0 ? 0 : op.o_valid) : O;
       rsrc = make_rsrc(op.base, static_cast<long long>(rows) * op.ld * 2);
       step = kSpan * 2;
@@ -375,19 +441,66 @@ struct DmaLoader {
     }
   }
 
-  // Issue the loads of call index i (a step, or a pair of steps) into `buf`.
-  __device__ __forceinline__ void issue(uint16_t* buf, int i) const {
+  // Gathered k-strided operand: load the row-map entries of call i into ring
+  // slot sl.  Every lane loads (a clamped index past the range), so each call
+  // issues the same number of loads, which the counted waits rely on.
+  __device__ __forceinline__ void fetch_rows(int i, int sl) {
+    if constexpr (GX && STRIDED) {
+#pragma unroll
+      for (int q = 0; q < kPerWave; ++q) {
+        const int r = min(g_lo + i * kBK + grow[q], g_hi - 1);
+        ring[q][sl] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(
+            g_rs, static_cast<unsigned>(r < 0 ? 0 : r) * 4u, 0, 0));
+      }
+    }
+  }
+
+  // Gathered k-strided operand: turn ring slot sl (row-map entries, landed)
+  // into physical rows.  Called at the start of the step that issues from
+  // that slot, so the division runs beside the MFMAs instead of in front of
+  // the loads.
+  __device__ __forceinline__ void prepare(int sl) {
+    if constexpr (GX && STRIDED) {
+      if (g_shift >= 0) {  // uniform: a power-of-two divisor is a shift
+#pragma unroll
+        for (int q = 0; q < kPerWave; ++q) ring[q][sl] = ring[q][sl] >> g_shift;
+      } else {
+#pragma unroll
+        for (int q = 0; q < kPerWave; ++q) ring[q][sl] = div_rows(ring[q][sl], g_div, g_magic);
+      }
+      // Pin the results here: otherwise the compiler sinks the division to
+      // just before the load that uses it, after the step's barrier.
+#pragma unroll
+      for (int q = 0; q < kPerWave; ++q) asm volatile("" : "+v"(ring[q][sl]));
+    }
+  }
+
+  // Issue the loads of call index i (a step, or a pair of steps) into `buf`;
+  // sl = i % 4, a compile-time constant at every call site (gathered
+  // k-strided operand: the ring slot holding call i's rows, refilled with
+  // those of call i + 4).
+  __device__ __forceinline__ void issue(uint16_t* buf, int i, int sl = 0) {
     if (kTotal < NW && static_cast<int>(threadIdx.x / kWave) >= kTotal) return;
 #pragma unroll
     for (int q = 0; q < kPerWave; ++q) {
       unsigned off;
-      if constexpr (STRIDED)
+      if constexpr (GX && STRIDED) {
+        const int r = g_lo + i * kBK + grow[q];
+        const int prow = ring[q][sl];  // prepared
+        // prow < 2^24 and the row stride < 2^24 bytes (checked on the host):
+        // a full-rate 24-bit multiply.
+        off = (r < g_hi && voff[q] != kOOB)
+                  ? voff[q] + __umul24(static_cast<unsigned>(prow), ld_bytes)
+                  : kOOB;
+      } else if constexpr (STRIDED) {
         off = voff[q] + static_cast<unsigned>(i) * step;
-      else
+      } else {
         off = i < klim ? voff[q] + static_cast<unsigned>(i) * step : kOOB;
+      }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(buf + lds_off[q]), 16, off, 0,
                                                0, 0);
     }
+    if constexpr (GX && STRIDED) fetch_rows(i + 4, sl);
   }
 };
 
@@ -493,14 +606,14 @@ __device__ __forceinline__ void mfma_step(f32x16 (&acc)[MI][NI], const Frags<MI,
 // ((t - 1) / 2) % 2 -- two steps ahead of the quad loads of step t - 1, since a
 // pair buffer frees up only after both steps of the pair it held.
 template <bool XS, bool YS, class XL, class YL>
-__device__ __forceinline__ void issue_step(const XL& xl, const YL& yl, const Bufs& xb,
-                                           const Bufs& yb, int s, int t) {
+__device__ __forceinline__ void issue_step(XL& xl, YL& yl, const Bufs& xb, const Bufs& yb, int s,
+                                           int t) {
   if ((s & 1) == 1) {
     if constexpr (!XS) xl.issue(xb.b[(s >> 1) & 1], t >> 1);
     if constexpr (!YS) yl.issue(yb.b[(s >> 1) & 1], t >> 1);
   }
-  if constexpr (XS) xl.issue(xb.b[s & 3], t);
-  if constexpr (YS) yl.issue(yb.b[s & 3], t);
+  if constexpr (XS) xl.issue(xb.b[s & 3], t, s & 3);
+  if constexpr (YS) yl.issue(yb.b[s & 3], t, s & 3);
 }
 
 // Scheduling pattern for a half step: each MFMA followed by up to two LDS
@@ -533,15 +646,18 @@ __device__ __forceinline__ void interleave_mfma_ds() {
 // outstanding.  Steps past the reduction range load zeros; the loop runs a
 // multiple of 4 steps.
 template <int MIV, bool XS, bool YS, int MI, int NI, class XL, class YL, class XA, class YA>
-__device__ __forceinline__ void reduce_tile(f32x16 (&acc)[MI][NI], const XL& xl, const YL& yl,
+__device__ __forceinline__ void reduce_tile(f32x16 (&acc)[MI][NI], XL& xl, YL& yl,
                                             const XA& xa, const YA& ya, const Bufs& xb,
                                             const Bufs& yb, int nk) {
-  constexpr int LQ = (XS ? XL::kPerWave : 0) + (YS ? YL::kPerWave : 0);  // per quad step
-  constexpr int LP = (XS ? 0 : XL::kPerWave) + (YS ? 0 : YL::kPerWave);  // per pair
+  constexpr int LQ = (XS ? XL::kLoadsPerCall : 0) + (YS ? YL::kLoadsPerCall : 0);  // per quad step
+  constexpr int LP = (XS ? 0 : XL::kLoadsPerCall) + (YS ? 0 : YL::kLoadsPerCall);  // per pair
   // Prologue: steps 0..3 in flight (pairs 0 and 1 with steps 1 and 3), step
   // 0 landed everywhere.
 #pragma unroll
-  for (int s = 0; s < 4; ++s) issue_step<XS, YS>(xl, yl, xb, yb, s, s);
+  for (int s = 0; s < 4; ++s) {
+    xl.prepare(s);
+    issue_step<XS, YS>(xl, yl, xb, yb, s, s);
+  }
   wait_vmcnt<3 * LQ + LP>();
   __builtin_amdgcn_s_barrier();
   Frags<MI, NI> f0, f1;
@@ -549,6 +665,7 @@ __device__ __forceinline__ void reduce_tile(f32x16 (&acc)[MI][NI], const XL& xl,
   for (int kt = 0; kt < nk; kt += 4) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      xl.prepare(s);  // gathered x: rows of the call this step issues
       read_frags<MIV, XS, YS>(f1, xb, yb, s, 1, xa, ya);
       mfma_step<MIV>(acc, f0);
       interleave_mfma_ds<MIV * NI>();
@@ -576,7 +693,10 @@ __device__ __forceinline__ void reduce_tile(f32x16 (&acc)[MI][NI], const XL& xl,
 // interleaved 32-column blocks of gate and up weights for 128 hidden units
 // (see Operand), so every wave holds the gate and the up value of the same
 // units in the same lanes; the epilogue stores h and act = silu(g) * u.
-template <int MODE, int BM, int BN, int WGM, int WGN, typename OutT, bool GLU = false>
+// GX: the x operand is gathered through p.xrows (GEMM 1 with the SwiGLU
+// epilogue, and the weight gradient).
+template <int MODE, int BM, int BN, int WGM, int WGN, typename OutT, bool GLU = false,
+          bool GX = false>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p) {
   constexpr bool XS = (MODE == kTN);  // x operand k-strided in memory
   constexpr bool YS = (MODE != kNT);  // y operand k-strided in memory
@@ -585,6 +705,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
   constexpr int MI = WM / 32, NI = WN / 32;
   static_assert(!GLU || (MODE == kNN && NI == 2 && sizeof(OutT) == 2),
                 "the SwiGLU epilogue pairs a wave's two column blocks");
+  static_assert(!GX || GLU || MODE == kTN, "gathered x: GEMM 1 with SwiGLU, weight gradient");
   // Elements per buffer: four quad buffers (k-strided) or two pair buffers.
   constexpr int XBE = XS ? BM * kBK : BM * 2 * kBK;
   constexpr int YBE = YS ? BN * kBK : BN * 2 * kBK;
@@ -617,8 +738,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
   Operand xo{}, yo{};
   if constexpr (GLU) {
     const int F = p.N / 2;
-    xo = {static_cast<const uint16_t*>(p.x) + static_cast<long long>(t.i0) * p.K, p.K,
-          t.g1 - t.i0, 0, 0};
+    if constexpr (GX)
+      xo = {static_cast<const uint16_t*>(p.x), p.K, t.g1 - t.i0, 0, 0, p.xrows + t.i0, p.xdiv,
+            p.xphys, 0, p.xmagic, p.xshift};
+    else
+      xo = {static_cast<const uint16_t*>(p.x) + static_cast<long long>(t.i0) * p.K, p.K,
+            t.g1 - t.i0, 0, 0};
     yo = {static_cast<const uint16_t*>(p.y) + t.e * KN, p.N, F - j0, F, j0};
   } else if constexpr (MODE == kNN) {
     xo = {static_cast<const uint16_t*>(p.x) + static_cast<long long>(t.i0) * p.K, p.K,
@@ -629,13 +754,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
           t.g1 - t.i0, 0, 0};
     yo = {static_cast<const uint16_t*>(p.y) + t.e * KN + static_cast<long long>(j0) * p.N, p.N,
           p.K - j0, 0, 0};
+  } else if constexpr (GX) {
+    xo = {static_cast<const uint16_t*>(p.x), p.K, p.K - t.i0, 0, 0, p.xrows, p.xdiv, p.xphys,
+          t.i0, p.xmagic, p.xshift};
+    yo = {static_cast<const uint16_t*>(p.y) + static_cast<long long>(t.r_lo) * p.N + j0, p.N,
+          p.N - j0, 0, 0};
   } else {
     xo = {static_cast<const uint16_t*>(p.x) + static_cast<long long>(t.r_lo) * p.K + t.i0, p.K,
           p.K - t.i0, 0, 0};
     yo = {static_cast<const uint16_t*>(p.y) + static_cast<long long>(t.r_lo) * p.N + j0, p.N,
           p.N - j0, 0, 0};
   }
-  DmaLoader<XS, BM, NW> xl;
+  DmaLoader<XS, BM, NW, GX> xl;
   DmaLoader<YS, BN, NW> yl;
   xl.init(xo, t.r_lo, t.r_hi);
   yl.init(yo, t.r_lo, t.r_hi);
@@ -984,14 +1114,15 @@ bool mfma_ok(moe_dtype dt, int M, int K, int N) {
 // 16-byte boundaries (null pointers pass).
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; }
 
-template <int MODE, int BM, int BN, int WGM, int WGN, typename OutT, bool GLU = false>
+template <int MODE, int BM, int BN, int WGM, int WGN, typename OutT, bool GLU = false,
+          bool GX = false>
 void launch_mfma(GemmArgs p, long long tiles_upper, hipStream_t st) {
   const long long grid = ceil_div(tiles_upper, 8) * 8;
-  hipLaunchKernelGGL((gemm_mfma_kernel<MODE, BM, BN, WGM, WGN, OutT, GLU>),
+  hipLaunchKernelGGL((gemm_mfma_kernel<MODE, BM, BN, WGM, WGN, OutT, GLU, GX>),
                      dim3(static_cast<unsigned>(grid)), dim3(64 * WGM * WGN), 0, st, p);
 }
 
-template <int MODE, typename OutT>
+template <int MODE, typename OutT, bool GX = false>
 void dispatch_mfma(Cfg c, GemmArgs p, hipStream_t st) {
   const int ncols = (MODE == kNN) ? p.N : (MODE == kNT ? p.K : p.N);
   p.ntn = static_cast<int>(ceil_div(ncols, c.bn));
@@ -1004,10 +1135,10 @@ void dispatch_mfma(Cfg c, GemmArgs p, hipStream_t st) {
   } else {
     upper = (ceil_div(p.M, c.bm) + p.E) * p.ntn;
   }
-  if (c.bm == 256 && c.bn == 256) launch_mfma<MODE, 256, 256, 2, 4, OutT>(p, upper, st);
-  else if (c.bm == 128 && c.bn == 128) launch_mfma<MODE, 128, 128, 2, 2, OutT>(p, upper, st);
-  else if (c.bm == 64 && c.bn == 256) launch_mfma<MODE, 64, 256, 1, 4, OutT>(p, upper, st);
-  else launch_mfma<MODE, 64, 64, 2, 2, OutT>(p, upper, st);
+  if (c.bm == 256 && c.bn == 256) launch_mfma<MODE, 256, 256, 2, 4, OutT, false, GX>(p, upper, st);
+  else if (c.bm == 128 && c.bn == 128) launch_mfma<MODE, 128, 128, 2, 2, OutT, false, GX>(p, upper, st);
+  else if (c.bm == 64 && c.bn == 256) launch_mfma<MODE, 64, 256, 1, 4, OutT, false, GX>(p, upper, st);
+  else launch_mfma<MODE, 64, 64, 2, 2, OutT, false, GX>(p, upper, st);
 }
 
 // GEMM 1 with the SwiGLU epilogue: tiles of 128 hidden units (gate and up
@@ -1017,15 +1148,16 @@ Cfg pick_glu_cfg(int M, int E, int N) {
   return c.bn == 64 ? Cfg{128, 128} : c;
 }
 
+template <bool GX = false>
 void dispatch_glu(Cfg c, GemmArgs p, hipStream_t st) {
   p.ntn = static_cast<int>(ceil_div(p.N / 2, c.bn / 2));
   const long long upper = (ceil_div(p.M, c.bm) + p.E) * p.ntn;
   if (c.bm == 256 && c.bn == 256)
-    launch_mfma<kNN, 256, 256, 2, 4, uint16_t, true>(p, upper, st);
+    launch_mfma<kNN, 256, 256, 2, 4, uint16_t, true, GX>(p, upper, st);
   else if (c.bm == 64 && c.bn == 256)
-    launch_mfma<kNN, 64, 256, 1, 4, uint16_t, true>(p, upper, st);
+    launch_mfma<kNN, 64, 256, 1, 4, uint16_t, true, GX>(p, upper, st);
   else
-    launch_mfma<kNN, 128, 128, 2, 2, uint16_t, true>(p, upper, st);
+    launch_mfma<kNN, 128, 128, 2, 2, uint16_t, true, GX>(p, upper, st);
 }
 
 template <int MODE, typename InT, typename OutT>
@@ -1044,6 +1176,36 @@ void launch_simt(GemmArgs p, hipStream_t st) {
   const long long grid = ceil_div(upper, 8) * 8;
   hipLaunchKernelGGL((gemm_simt_kernel<MODE, InT, OutT>), dim3(static_cast<unsigned>(grid)),
                      dim3(kThreads), 0, st, p);
+}
+
+// Row map of a gathered operand: logical row p is physical row rows[p] / div
+// of an array of `phys` rows of `ld` elements.  The MFMA loaders address it
+// with 32-bit byte offsets.
+// ceil(2^32 / d) mod 2^32 for div_rows.
+unsigned div_magic(int d) {
+  const unsigned long long dd = static_cast<unsigned long long>(d < 1 ? 1 : d);
+  return static_cast<unsigned>(((1ull << 32) + dd - 1) / dd);
+}
+
+// log2(d) for a power of two d, else -1.
+int div_shift(int d) {
+  if (d < 1 || (d & (d - 1)) != 0) return -1;
+  int s = 0;
+  while ((1 << s) < d) ++s;
+  return s;
+}
+
+moe_status check_gather(const char* fn, const int32_t* rows, int div, int phys, int ld) {
+  (void)fn;
+  MOE_REQUIRE(rows != nullptr, MOE_ERR_INVALID_ARG, "gathered operand: null row map");
+  MOE_REQUIRE(div >= 1 && phys >= 1, MOE_ERR_INVALID_ARG,
+              "gathered operand: row divisor and physical rows must be >= 1");
+  MOE_REQUIRE(static_cast<long long>(phys) * ld < (1ll << 30) && phys < (1 << 24) &&
+                  ld < (1 << 23),
+              MOE_ERR_UNSUPPORTED,
+              "gathered operand: needs physical rows * row length < 2^30, rows < 2^24 and row "
+              "length < 2^23");
+  return MOE_OK;
 }
 
 moe_status check_gemm(const void* offsets, int M, int K, int N, int E, moe_dtype dt) {
@@ -1133,6 +1295,29 @@ extern "C" moe_status moe_grouped_gemm_swiglu_fwd(const void* a, const void* b,
   return moe_act_fwd(h, M, F, dtype, act, stream);
 }
 
+extern "C" moe_status moe_grouped_gemm_swiglu_fwd_gather(
+    const void* x, const int32_t* x_rows, int x_div, int x_phys, const void* b,
+    const int32_t* offsets, int M, int K, int F, int E, moe_dtype dtype, void* h, void* act,
+    moe_stream_t stream) {
+  clear_error();
+  MOE_REQUIRE(F >= 1 && F <= (1 << 29), MOE_ERR_INVALID_ARG,
+              "moe_grouped_gemm_swiglu_fwd_gather: F out of range");
+  const int N = 2 * F;
+  if (moe_status s = check_gemm(offsets, M, K, N, E, dtype)) return s;
+  MOE_REQUIRE(x && b && h && act, MOE_ERR_INVALID_ARG,
+              "moe_grouped_gemm_swiglu_fwd_gather: null pointer");
+  if (moe_status s = check_gather("moe_grouped_gemm_swiglu_fwd_gather", x_rows, x_div, x_phys, K))
+    return s;
+  MOE_REQUIRE(F % 8 == 0 && mfma_ok(dtype, M, K, N), MOE_ERR_UNSUPPORTED,
+              "moe_grouped_gemm_swiglu_fwd_gather: needs the bf16 MFMA path (K, F multiples of 8)");
+  MOE_REQUIRE(aligned16(x) && aligned16(b) && aligned16(h) && aligned16(act), MOE_ERR_INVALID_ARG,
+              "moe_grouped_gemm_swiglu_fwd_gather: operands and results must be 16-byte aligned");
+  GemmArgs p{x, b, nullptr, h, offsets, M, K, N, E, 0, 0, 1, act, x_rows, x_div, x_phys,
+             div_magic(x_div), div_shift(x_div)};
+  dispatch_glu<true>(pick_glu_cfg(M, E, N), p, as_stream(stream));
+  return check_launch("moe_grouped_gemm_swiglu_fwd_gather");
+}
+
 extern "C" moe_status moe_grouped_gemm_fwd(const void* a, const void* b, const int32_t* offsets,
                                            int M, int K, int N, int E, moe_dtype ab_dtype,
                                            void* c, moe_dtype c_dtype, void* ws, size_t ws_bytes,
@@ -1163,12 +1348,13 @@ extern "C" moe_status moe_grouped_gemm_fwd(const void* a, const void* b, const i
   return check_launch("moe_grouped_gemm_fwd");
 }
 
-extern "C" moe_status moe_grouped_gemm_bwd(const void* a, const void* b, const void* dc,
-                                           const int32_t* offsets, int M, int K, int N, int E,
-                                           moe_dtype dtype, void* da, const void* da_add,
-                                           float* db, void* ws, size_t ws_bytes,
-                                           moe_stream_t stream) {
-  clear_error();
+namespace moe {
+namespace {
+
+moe_status grouped_gemm_bwd(const void* a, const int32_t* a_rows, int a_div, int a_phys,
+                            const void* b, const void* dc, const int32_t* offsets, int M, int K,
+                            int N, int E, moe_dtype dtype, void* da, const void* da_add,
+                            float* db, void* ws, size_t ws_bytes, moe_stream_t stream) {
   if (moe_status s = check_gemm(offsets, M, K, N, E, dtype)) return s;
   MOE_REQUIRE(dc != nullptr, MOE_ERR_INVALID_ARG, "moe_grouped_gemm_bwd: null dc");
   MOE_REQUIRE(da == nullptr || b != nullptr, MOE_ERR_INVALID_ARG,
@@ -1207,8 +1393,12 @@ extern "C" moe_status moe_grouped_gemm_bwd(const void* a, const void* b, const v
   if (db) {
     if (use_mfma) {
       GemmArgs p{a, dc, nullptr, split > 1 ? ws : static_cast<void*>(db), offsets, M, K, N, E,
-                 0, 0, split};
-      dispatch_mfma<kTN, float>(pick_tn_cfg(K, N, E), p, st);
+                 0, 0, split, nullptr, a_rows, a_div, a_phys, div_magic(a_div),
+                 div_shift(a_div)};
+      if (a_rows)
+        dispatch_mfma<kTN, float, true>(pick_tn_cfg(K, N, E), p, st);
+      else
+        dispatch_mfma<kTN, float>(pick_tn_cfg(K, N, E), p, st);
       if (moe_status s = check_launch("moe_grouped_gemm_bwd/db")) return s;
       if (split > 1) {
         const long long n = static_cast<long long>(E) * K * N;
@@ -1225,4 +1415,32 @@ extern "C" moe_status moe_grouped_gemm_bwd(const void* a, const void* b, const v
     if (moe_status s = check_launch("moe_grouped_gemm_bwd/db")) return s;
   }
   return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status moe_grouped_gemm_bwd(const void* a, const void* b, const void* dc,
+                                           const int32_t* offsets, int M, int K, int N, int E,
+                                           moe_dtype dtype, void* da, const void* da_add,
+                                           float* db, void* ws, size_t ws_bytes,
+                                           moe_stream_t stream) {
+  clear_error();
+  return grouped_gemm_bwd(a, nullptr, 1, 0, b, dc, offsets, M, K, N, E, dtype, da, da_add, db, ws,
+                          ws_bytes, stream);
+}
+
+extern "C" moe_status moe_grouped_gemm_bwd_gather(const void* a, const int32_t* a_rows,
+                                                  int a_div, int a_phys, const void* b,
+                                                  const void* dc, const int32_t* offsets, int M,
+                                                  int K, int N, int E, moe_dtype dtype, void* da,
+                                                  const void* da_add, float* db, void* ws,
+                                                  size_t ws_bytes, moe_stream_t stream) {
+  clear_error();
+  if (moe_status s = check_gather("moe_grouped_gemm_bwd_gather", a_rows, a_div, a_phys, K))
+    return s;
+  MOE_REQUIRE(mfma_ok(dtype, M, K, N), MOE_ERR_UNSUPPORTED,
+              "moe_grouped_gemm_bwd_gather: needs the bf16 MFMA path (K, N multiples of 8)");
+  return grouped_gemm_bwd(a, a_rows, a_div, a_phys, b, dc, offsets, M, K, N, E, dtype, da, da_add,
+                          db, ws, ws_bytes, stream);
 }

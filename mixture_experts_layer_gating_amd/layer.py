@@ -58,7 +58,7 @@ class MoELayer:
     """
 
     def __init__(self, T, d, E, k, F, dtype=torch.bfloat16, device="cuda", renorm=False,
-                 fuse_act=True, overlap_wgrad=False):
+                 fuse_act=True, overlap_wgrad=False, gather_x=True):
         if not (1 <= k <= E):
             raise ValueError("need 1 <= k <= E")
         self.T, self.d, self.E, self.k, self.F = T, d, E, k, F
@@ -67,6 +67,10 @@ class MoELayer:
         self.renorm = bool(renorm)
         self.fuse_act = bool(fuse_act)
         self.overlap_wgrad = bool(overlap_wgrad)
+        # GEMM 1 and its weight gradient read x through the row map src / k
+        # instead of a permuted copy (bf16, fused activation, MFMA shapes).
+        plan = L.moe_grouped_gemm_plan(3, T * k, d, 2 * F, E, self.code)
+        self.gather_x = bool(gather_x) and self.fuse_act and bool(plan["mfma"])
         self.device = torch.device(device)
         Tk = T * k
         self.Tk = Tk
@@ -140,9 +144,14 @@ class MoELayer:
         with self._span("count_index"):
             L.moe_count_index(self.idx, T, k, E, self.counts, self.offsets, self.dest, self.src,
                               self.ci_ws, self.ci_ws.numel(), stream=s)
-        with self._span("permute"):
-            L.moe_permute(x, self.dest, T, k, d, c, self.xp, stream=s)
-        if self.fuse_act:
+        if not self.gather_x:
+            with self._span("permute"):
+                L.moe_permute(x, self.dest, T, k, d, c, self.xp, stream=s)
+        if self.gather_x:
+            with self._span("gemm1_swiglu_fwd"):
+                L.moe_grouped_gemm_swiglu_fwd_gather(x, self.src, k, T, w1, self.offsets, Tk, d,
+                                                     F, E, c, self.h, self.a, stream=s)
+        elif self.fuse_act:
             with self._span("gemm1_swiglu_fwd"):
                 L.moe_grouped_gemm_swiglu_fwd(self.xp, w1, self.offsets, Tk, d, F, E, c, self.h,
                                               self.a, stream=s)
@@ -159,6 +168,17 @@ class MoELayer:
             L.moe_unpermute(self.yp, self.dest, self.w, T, k, d, c, self.y, stream=s)
         self._inputs = (x, wr, w1, w2)
         return self.y
+
+    def _dw1(self, x, w1, ws, wsb, stream):
+        """dW1 = xp^T @ dh, with xp read from x through src / k when gathering."""
+        T, d, E, k, F, Tk, c = self.T, self.d, self.E, self.k, self.F, self.Tk, self.code
+        if self.gather_x:
+            L.moe_grouped_gemm_bwd_gather(x, self.src, k, T, w1, self.dh, self.offsets, Tk, d,
+                                          2 * F, E, c, None, None, self.dw1, ws, wsb,
+                                          stream=stream)
+        else:
+            L.moe_grouped_gemm_bwd(self.xp, w1, self.dh, self.offsets, Tk, d, 2 * F, E, c, None,
+                                   None, self.dw1, ws, wsb, stream=stream)
 
     def backward(self, dy, stream=None):
         if self._inputs is None:
@@ -192,8 +212,7 @@ class MoELayer:
                                            None, None, self.dw2, ws2, wsb, stream=side)
                 side.wait_event(self.ev_dh)
                 with self._span("gemm1_bwd_dw"):
-                    L.moe_grouped_gemm_bwd(self.xp, w1, self.dh, self.offsets, Tk, d, 2 * F, E,
-                                           c, None, None, self.dw1, ws2, wsb, stream=side)
+                    self._dw1(x, w1, ws2, wsb, side)
             self.ev_side.record(side)
         else:
             with self._span("gemm2_bwd_dw"):
@@ -206,8 +225,7 @@ class MoELayer:
             L.moe_unpermute(self.dxp, self.dest, None, T, k, d, c, self.dx_e, stream=main)
         if not overlap:
             with self._span("gemm1_bwd_dw"):
-                L.moe_grouped_gemm_bwd(self.xp, w1, self.dh, self.offsets, Tk, d, 2 * F, E, c,
-                                       None, None, self.dw1, ws, wsb, stream=main)
+                self._dw1(x, w1, ws, wsb, main)
         with self._span("route_topk_bwd"):
             L.moe_route_topk_bwd(self.probs, self.idx, self.dw, T, E, k, self.renorm,
                                  self.dlogits, c, stream=main)

@@ -97,3 +97,36 @@ def test_gemm_validation_and_workspace():
     assert _rc("moe_grouped_gemm_fwd", FAKE, FAKE, FAKE, 4, 8, 8, 1, L.MOE_BF16, odd, L.MOE_F32, None, 0, None) == L.MOE_ERR_INVALID_ARG
     assert _rc("moe_grouped_gemm_bwd", FAKE, FAKE, FAKE, FAKE, 16, 8, 8, 1, L.MOE_BF16, odd, None, None, None, 0, None) == L.MOE_ERR_INVALID_ARG
     assert _rc("moe_grouped_gemm_bwd", FAKE, FAKE, FAKE, FAKE, 16, 8, 8, 1, L.MOE_BF16, FAKE, odd, None, None, 0, None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_gathered_gemm_validation():
+    # swiglu_fwd_gather(x, x_rows, x_div, x_phys, b, offsets, M, K, F, E, dtype, h, act, stream)
+    ok = (FAKE, FAKE, 8, 64, FAKE, FAKE, 512, 64, 32, 4, L.MOE_BF16, FAKE, FAKE, None)
+    def sw(**kw):
+        args = list(ok)
+        for i, v in kw.items():
+            args[int(i[1:])] = v
+        return _rc("moe_grouped_gemm_swiglu_fwd_gather", *args)
+    assert sw(a1=None) == L.MOE_ERR_INVALID_ARG          # null row map
+    assert sw(a2=0) == L.MOE_ERR_INVALID_ARG             # divisor < 1
+    assert sw(a3=0) == L.MOE_ERR_INVALID_ARG             # no physical rows
+    assert sw(a3=1 << 24) == L.MOE_ERR_UNSUPPORTED       # rows past 24 bits
+    assert sw(a8=36) == L.MOE_ERR_UNSUPPORTED            # F not a multiple of 8
+    assert sw(a10=L.MOE_F32) == L.MOE_ERR_UNSUPPORTED    # float32: no MFMA path
+    assert sw(a0=FAKE + 8) == L.MOE_ERR_INVALID_ARG      # misaligned x
+    assert sw(a0=None) == L.MOE_ERR_INVALID_ARG
+    # bwd_gather(a, a_rows, a_div, a_phys, b, dc, offsets, M, K, N, E, dtype, da, da_add, db,
+    #            ws, ws_bytes, stream)
+    okb = (FAKE, FAKE, 8, 64, FAKE, FAKE, FAKE, 512, 64, 64, 4, L.MOE_BF16, None, None, FAKE,
+           None, 0, None)
+    def bw(**kw):
+        args = list(okb)
+        for i, v in kw.items():
+            args[int(i[1:])] = v
+        return _rc("moe_grouped_gemm_bwd_gather", *args)
+    assert bw(a1=None) == L.MOE_ERR_INVALID_ARG
+    assert bw(a2=-1) == L.MOE_ERR_INVALID_ARG
+    assert bw(a3=1 << 20, a8=2048) == L.MOE_ERR_UNSUPPORTED  # physical rows * K >= 2^30
+    assert bw(a8=12) == L.MOE_ERR_UNSUPPORTED            # K not a multiple of 8
+    assert bw(a11=L.MOE_F32) == L.MOE_ERR_UNSUPPORTED
+    assert bw(a14=FAKE + 4) == L.MOE_ERR_INVALID_ARG     # misaligned db

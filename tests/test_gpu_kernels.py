@@ -254,3 +254,53 @@ def test_grouped_gemm_swiglu(M, K, F, E, pattern, dtype):
     # act is computed from the stored h: exactly what the activation kernel gives
     np.testing.assert_array_equal(bits(act)[rows], bits(act2)[rows])
     assert rel(host(act)[rows], O.swiglu(ref_h)[rows]) <= 2 * tol
+
+
+# ------------------------------------------------------------------ gathered operands
+# (T, k, d, F, E, pattern): k = 8 and 2 take the shift path of the row-map
+# division, k = 3 and 5 the multiply-high path; E = 1 with few rows takes the
+# sliced weight gradient.
+GATHER_CASES = [(1024, 8, 256, 128, 16, "random"), (700, 3, 264, 136, 5, "empty"),
+                (4096, 2, 512, 256, 8, "skew"), (333, 5, 128, 64, 7, "one"),
+                (2048, 1, 512, 64, 1, "uniform")]
+
+
+@pytest.mark.parametrize("T,k,d,F,E,pattern", GATHER_CASES)
+def test_grouped_gemm_gathered_x(T, k, d, F, E, pattern):
+    """GEMM 1 + SwiGLU and the weight gradient reading x through src / k give
+    the same bits as the plain calls on the permuted copy xp[p] = x[src[p] / k]
+    (rows of xp past the groups are never read)."""
+    say(f"grouped_gemm gathered x T={T} k={k} d={d} F={F} E={E} {pattern}")
+    bf, code = torch.bfloat16, L.MOE_BF16
+    M = T * k
+    off = _groups(M, E, pattern, 3)
+    src = np.random.default_rng(4).permutation(M).astype(np.int32)
+    x = _normal((T, d), 5)
+    w1 = _normal((E, d, 2 * F), 6, scale=0.05)
+    dh = _normal((M, 2 * F), 7)
+    xp = x[src // k]
+    xd, srcd, w1d, offd, dhd = dev(x, bf), dev(src), dev(w1, bf), dev(off), dev(dh, bf)
+    xpd = dev(xp, bf)
+    # forward: h, act
+    h0 = torch.zeros(M, 2 * F, dtype=bf, device=DEV)
+    a0 = torch.zeros(M, F, dtype=bf, device=DEV)
+    L.moe_grouped_gemm_swiglu_fwd(xpd, w1d, offd, M, d, F, E, code, h0, a0)
+    h1 = torch.zeros_like(h0)
+    a1 = torch.zeros_like(a0)
+    L.moe_grouped_gemm_swiglu_fwd_gather(xd, srcd, k, T, w1d, offd, M, d, F, E, code, h1, a1)
+    # weight gradient
+    nb = L.moe_grouped_gemm_workspace_size(M, d, 2 * F, E, code)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=DEV)
+    db0 = torch.full((E, d, 2 * F), 7.0, dtype=torch.float32, device=DEV)
+    db1 = torch.full_like(db0, -7.0)
+    L.moe_grouped_gemm_bwd(xpd, w1d, dhd, offd, M, d, 2 * F, E, code, None, None, db0, ws, nb)
+    L.moe_grouped_gemm_bwd_gather(xd, srcd, k, T, w1d, dhd, offd, M, d, 2 * F, E, code, None,
+                                  None, db1, ws, nb)
+    torch.cuda.synchronize()
+    rows = slice(0, int(off[-1]))
+    np.testing.assert_array_equal(bits(h1)[rows], bits(h0)[rows])
+    np.testing.assert_array_equal(bits(a1)[rows], bits(a0)[rows])
+    np.testing.assert_array_equal(host(db1), host(db0))
+    # and against the oracle
+    _, ref_db = O.grouped_matmul_backward(xp, w1, dh, off)
+    assert rel(host(db1), ref_db) <= TOL_F32
