@@ -71,16 +71,20 @@ struct GemmArgs {
 };
 
 // ------------------------------------------------------------------ tiles
-// Row-tiled modes (NN, NT): wave 0 finds which expert owns this workgroup's
-// row tile.  Tiles are counted per expert as ceil(rows_e / BM); logical tile
-// L = row_tile * ntn + col_tile; workgroup b runs on XCD b % 8 and takes
-// logical tile (b % 8) * ceil(n / 8) + b / 8.  Up to kHeld * 64 experts the
-// offsets are loaded once (all loads in flight together) and kept in
-// registers; the expert's row range goes back through sh[] so that no thread
-// reloads it.
+// Row-tiled modes (NN, NT): every wave finds which expert owns this
+// workgroup's row tile (the same answer in each wave, so no LDS and no
+// barrier are needed, and small tiles keep their LDS footprint at a multiple
+// of the operand buffers).  Tiles are counted per expert as
+// ceil(rows_e / BM); logical tile L = row_tile * ntn + col_tile; workgroup b
+// runs on XCD b % 8 and takes logical tile (b % 8) * ceil(n / 8) + b / 8.  Up
+// to kHeld * 64 experts the offsets are loaded once (all loads in flight
+// together) and kept in registers.
+struct RowTile {
+  int found, e, mt_local, nt, g0, g1;  // wave-uniform
+};
+
 template <int BM>
-__device__ void find_row_tile(const int32_t* __restrict__ offsets, int E, int ntn, int lane,
-                              int* sh) {
+__device__ RowTile find_row_tile(const int32_t* __restrict__ offsets, int E, int ntn, int lane) {
   constexpr int kHeld = 4;
   const bool held = E <= kHeld * kWave;
   int o0[kHeld], o1[kHeld], tiles[kHeld], incl[kHeld];
@@ -158,14 +162,7 @@ __device__ void find_row_tile(const int32_t* __restrict__ offsets, int E, int nt
       }
     }
   }
-  if (lane == 0) {
-    sh[0] = found;
-    sh[1] = e_found;
-    sh[2] = mt_local;
-    sh[3] = nt;
-    sh[4] = g0;
-    sh[5] = g1;
-  }
+  return RowTile{found, e_found, mt_local, nt, g0, g1};
 }
 
 struct TileInfo {
@@ -176,7 +173,7 @@ struct TileInfo {
 constexpr int kTnDeal = 2;  // weight-gradient tile rows dealt to an XCD at a time
 
 template <int MODE, int BM>
-__device__ bool resolve_tile(const GemmArgs& p, int* sh, TileInfo& t) {
+__device__ bool resolve_tile(const GemmArgs& p, TileInfo& t) {
   if constexpr (MODE == kTN) {
     // Tile rows (slice, e, row tile) are dealt over the XCDs in pairs --
     // XCD x takes rows 2x, 2x + 1, 2x + 16, 2x + 17, ... with all ntn column
@@ -213,14 +210,13 @@ __device__ bool resolve_tile(const GemmArgs& p, int* sh, TileInfo& t) {
     return true;
   } else {
     const int lane = threadIdx.x & (kWave - 1);
-    if (threadIdx.x < kWave) find_row_tile<BM>(p.offsets, p.E, p.ntn, lane, sh);
-    __syncthreads();
-    if (!sh[0]) return false;
-    t.e = sh[1];
-    t.g0 = sh[4];
-    t.g1 = sh[5];
-    t.i0 = t.g0 + sh[2] * BM;
-    t.j0 = sh[3];
+    const RowTile r = find_row_tile<BM>(p.offsets, p.E, p.ntn, lane);
+    if (!r.found) return false;
+    t.e = r.e;
+    t.g0 = r.g0;
+    t.g1 = r.g1;
+    t.i0 = t.g0 + r.mt_local * BM;
+    t.j0 = r.nt;
     t.r_lo = 0;
     t.r_hi = (MODE == kNN) ? p.K : p.N;
     t.slice = 0;
@@ -719,10 +715,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
   __shared__ __attribute__((aligned(1024))) uint16_t yb1[YBE];
   __shared__ alignas(YS ? 1024 : 16) uint16_t yb2[YS ? YBE : 8];
   __shared__ alignas(YS ? 1024 : 16) uint16_t yb3[YS ? YBE : 8];
-  __shared__ int sh[8];
 
   TileInfo t;
-  if (!resolve_tile<MODE, BM>(p, sh, t)) return;
+  if (!resolve_tile<MODE, BM>(p, t)) return;
   // The tile is the same for the whole workgroup; say so, so that buffer
   // descriptors built from it live in scalar registers.
   t.e = __builtin_amdgcn_readfirstlane(t.e);
@@ -951,9 +946,8 @@ template <int MODE, typename InT, typename OutT>
 __global__ __launch_bounds__(kThreads) void gemm_simt_kernel(GemmArgs p) {
   __shared__ float xs[kSimtBK][kSimtTile + 4];
   __shared__ float ys[kSimtBK][kSimtTile + 4];
-  __shared__ int sh[8];
   TileInfo t;
-  if (!resolve_tile<MODE, kSimtTile>(p, sh, t)) return;
+  if (!resolve_tile<MODE, kSimtTile>(p, t)) return;
   const int j0 = t.j0 * kSimtTile;
   const long long KN = static_cast<long long>(p.K) * p.N;
   const InT* X = static_cast<const InT*>(p.x);
