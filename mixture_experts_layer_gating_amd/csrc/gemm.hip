@@ -68,6 +68,7 @@ struct GemmArgs {
   int xphys;
   unsigned xmagic;  // ceil(2^32 / xdiv) mod 2^32 (see div_rows)
   int xshift;       // log2(xdiv) when xdiv is a power of two, else -1
+  int hot_first;    // TN, E <= 256: take the groups in hot-first order (group_at)
 };
 
 // ------------------------------------------------------------------ tiles
@@ -169,6 +170,48 @@ struct TileInfo {
   int e, i0, j0, r_lo, r_hi, g0, g1, slice;
 };
 
+// Weight-gradient tiles reduce over all rows of their group, so a hot group's
+// tiles are long; started last, they leave the other compute units idle at
+// the end of the launch.  Hot-first order: groups with at least 6, 4, 3, 2
+// and 1.5 times the mean row count, bucket by bucket, then the rest, by index
+// within a bucket (the longest tiles start first, without a sort).  Groups
+// below 1.5 times the mean keep their index order.  Returns the group at
+// position `pos` of that order; E <= 256.  Run by every wave (wave-uniform).
+__device__ int group_at(const int32_t* __restrict__ offsets, int E, int pos, int lane) {
+  constexpr int kRuns = 4;                          // runs of 64 groups
+  constexpr int kTimes2[] = {12, 8, 6, 4, 3};       // bucket bounds, x2
+  constexpr int kBuckets = 6;
+  const long long total = offsets[E] - offsets[0];  // all rows (uniform)
+  int bucket[kRuns];
+#pragma unroll
+  for (int c = 0; c < kRuns; ++c) {
+    const int e = c * kWave + lane;
+    bucket[c] = -1;  // past E: in no bucket
+    if (e < E) {
+      const long long n2e = 2ll * (offsets[e + 1] - offsets[e]) * E;  // 2 n_e E vs th2 * total
+      int b = kBuckets - 1;
+#pragma unroll
+      for (int q = kBuckets - 2; q >= 0; --q)
+        if (n2e >= kTimes2[q] * total) b = q;
+      bucket[c] = b;
+    }
+  }
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int b = 0; b < kBuckets; ++b) {
+#pragma unroll
+    for (int c = 0; c < kRuns; ++c) {
+      const uint64_t m = __ballot(bucket[c] == b);
+      const int cnt = __popcll(m);
+      if (pos < cnt) {
+        const bool hit = bucket[c] == b && __popcll(m & below) == pos;
+        return c * kWave + __builtin_ctzll(__ballot(hit));
+      }
+      pos -= cnt;
+    }
+  }
+  return 0;  // pos >= E: not reached (callers pass pos < E)
+}
+
 // Returns false if this workgroup has no tile.  Must be called by all threads.
 constexpr int kTnDeal = 2;  // weight-gradient tile rows dealt to an XCD at a time
 
@@ -194,8 +237,9 @@ __device__ bool resolve_tile(const GemmArgs& p, TileInfo& t) {
     const long long per_slice = per_e * p.E;
     t.slice = static_cast<int>(L / per_slice);
     const long long rem0 = L - static_cast<long long>(t.slice) * per_slice;
-    t.e = static_cast<int>(rem0 / per_e);
-    const int rem = static_cast<int>(rem0 - static_cast<long long>(t.e) * per_e);
+    const int pos = static_cast<int>(rem0 / per_e);
+    const int rem = static_cast<int>(rem0 - static_cast<long long>(pos) * per_e);
+    t.e = p.hot_first ? group_at(p.offsets, p.E, pos, threadIdx.x & (kWave - 1)) : pos;
     const int mt = rem / p.ntn;
     const int nt = rem - mt * p.ntn;
     t.i0 = mt * BM;
@@ -1386,9 +1430,12 @@ moe_status grouped_gemm_bwd(const void* a, const int32_t* a_rows, int a_div, int
   }
   if (db) {
     if (use_mfma) {
+      // Hot-first group order for groups long enough that their tiles'
+      // lengths matter (at least 128 rows on average).
+      const int hot_first = split == 1 && E >= 2 && E <= 256 && M / E >= 128 ? 1 : 0;
       GemmArgs p{a, dc, nullptr, split > 1 ? ws : static_cast<void*>(db), offsets, M, K, N, E,
                  0, 0, split, nullptr, a_rows, a_div, a_phys, div_magic(a_div),
-                 div_shift(a_div)};
+                 div_shift(a_div), hot_first};
       if (a_rows)
         dispatch_mfma<kTN, float, true>(pick_tn_cfg(K, N, E), p, st);
       else

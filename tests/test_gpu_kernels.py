@@ -129,6 +129,7 @@ GEMM_CASES = [
     (777, 64, 128, 4, "one"),            # every row in the last group
     (333, 12, 20, 3, "random"),          # K, N not multiples of 8 -> FMA kernel
     (2400, 64, 128, 300, "random"),      # more groups than the tile scan keeps in registers
+    (8192, 1024, 1024, 16, "skew"),      # weight gradient in hot-first group order
 ]
 
 
