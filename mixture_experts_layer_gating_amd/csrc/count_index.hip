@@ -64,9 +64,21 @@ __global__ __launch_bounds__(kScanBlock) void ci_scan_kernel(const int32_t* __re
   const bool act = e < E;
   const int b0 = min(nblk, sub * per_t), b1 = min(nblk, b0 + per_t);
   const int32_t* row = blk_cnt + static_cast<size_t>(act ? e : 0) * nblk;
+  // A thread's block counts are loaded kBatch at a time, all in flight
+  // together (a loop of single loads waits once per block); runs of up to
+  // kBatch blocks (the common case: T*k <= 16 Ki slots per expert thread)
+  // keep them in registers for the second pass.
+  constexpr int kBatch = 8;
+  int held[kBatch];
   int part = 0;
-  if (act)
-    for (int b = b0; b < b1; ++b) part += row[b];
+  if (act) {
+    for (int b = b0; b < b1; b += kBatch) {
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) held[q] = b + q < b1 ? row[b + q] : 0;
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) part += held[q];
+    }
+  }
   // Inclusive scan over the expert's tpe threads, then its total.
   int inc = part;
   for (int o = 1; o < tpe; o <<= 1) {
@@ -96,9 +108,16 @@ __global__ __launch_bounds__(kScanBlock) void ci_scan_kernel(const int32_t* __re
     }
     int32_t* orow = blk_off + static_cast<size_t>(e) * nblk;
     int run = base + inc - part;
-    for (int b = b0; b < b1; ++b) {
-      orow[b] = run;
-      run += row[b];
+    for (int b = b0; b < b1; b += kBatch) {
+      if (b1 - b0 > kBatch) {  // reload this batch (held has the last one)
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) held[q] = b + q < b1 ? row[b + q] : 0;
+      }
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        if (b + q < b1) orow[b + q] = run;
+        run += held[q];
+      }
     }
   }
 }

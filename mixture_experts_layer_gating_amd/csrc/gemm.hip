@@ -1085,8 +1085,16 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
                                                            long long n, int split,
                                                            float* __restrict__ db) {
   for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += gridDim.x * 256LL) {
+    // Eight partials loaded at a time (all in flight), summed in slice order.
     float s = 0.f;
-    for (int q = 0; q < split; ++q) s += part[q * n + i];
+    for (int q0 = 0; q0 < split; q0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = q0 + q < split ? part[(q0 + q) * n + i] : 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q0 + q < split) s += v[q];
+    }
     db[i] = s;
   }
 }

@@ -74,12 +74,21 @@ SMALL = [
     dict(T=333, d=256, E=16, k=4, F=136),     # ragged everything
     dict(T=64, d=128, E=1, k=1, F=64),        # single expert: plain SwiGLU FFN
     dict(T=256, d=256, E=64, k=8, F=128),     # small groups, empty experts
+    dict(T=1, d=64, E=4, k=4, F=32),          # one token, every expert selected (k = E)
+    dict(T=37, d=72, E=5, k=1, F=40),         # top-1, widths not multiples of 64
 ]
 
 
 @pytest.mark.parametrize("shape", SMALL)
 def test_layer_small_bf16(shape):
     wl = Workload("small", dtype="bf16", w_std=0.05, seed=sum(shape.values()), **shape)
+    say(f"layer {wl}")
+    _full_compare(make_inputs(wl))
+
+
+def test_layer_ragged_fp32():
+    # float32 at widths off the MFMA path (FMA kernels throughout)
+    wl = Workload("ragged", T=100, d=40, E=6, k=3, F=24, dtype="fp32", w_std=0.05, seed=5)
     say(f"layer {wl}")
     _full_compare(make_inputs(wl))
 
