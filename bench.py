@@ -430,6 +430,28 @@ def main():
     g_ms = sum(kernels[n]["ms"] for n in EXPERT_GEMMS)
     gemm_frac = g_fl / (g_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
 
+    # Context for the MFMA roofline: what a plain library GEMM (torch.matmul,
+    # hipBLASLt) sustains on this machine for a large square bf16 product.
+    ref_gemm = None
+    if wl.dtype == "bf16":
+        n = 8192
+        ga = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        gb = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(ga, gb)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            torch.matmul(ga, gb)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        ref_gemm = {"what": "torch.matmul (hipBLASLt) bf16 8192 x 8192 x 8192",
+                    "tflops": round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1),
+                    "frac_of_peak": round(2 * n ** 3 / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del ga, gb
+
     if args.copy_probe:
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -452,6 +474,7 @@ def main():
         "grouped_gemm_frac_of_bf16_peak": round(gemm_frac, 4),
         "grouped_gemm_tflops": round(g_fl / (g_ms * 1e-3) / 1e12, 1),
         "roofline": roofline,
+        "library_gemm_reference": ref_gemm,
         "kernels": kernels,
         "kernels_note": f"per-call times from {n_brk} steps after the timed region",
     }
