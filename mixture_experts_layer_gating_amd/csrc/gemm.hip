@@ -28,9 +28,10 @@
 // valid rows (GEMM 1 can apply SwiGLU there).  Workgroups are mapped so that
 // each of the 8 XCDs (own L2) walks a contiguous range of tiles, which keeps
 // one expert's weights and rows in one L2; weight-gradient tile rows are
-// dealt over the XCDs in pairs (balance under skewed routing).  Shapes with
-// few output tiles reduce the weight gradient in row slices (partials in a
-// workspace, summed in slice order).
+// dealt over the XCDs in pairs, the hottest experts' first (balance under
+// skewed routing: a weight-gradient tile is as long as its expert's row
+// count).  Shapes with few output tiles reduce the weight gradient in row
+// slices (partials in a workspace, summed in slice order).
 //
 // Float32 (and shapes whose K or N is not a multiple of 8) run on a plain
 // LDS-tiled FMA kernel (gemm_simt_kernel) with the same tile resolution.
