@@ -35,7 +35,8 @@ def _normal(shape, seed, scale=1.0, dtype="bf16"):
 
 # ------------------------------------------------------------------ permute / combine
 @pytest.mark.parametrize("T,k,E,d", [(1, 1, 1, 8), (37, 2, 5, 24), (1024, 8, 64, 2048),
-                                     (300, 3, 7, 136), (50, 10, 16, 64), (20, 32, 40, 32)])
+                                     (300, 3, 7, 136), (50, 10, 16, 64), (20, 32, 40, 32),
+                                     (96, 8, 32, 4096), (33, 3, 6, 4104)])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_permute_unpermute(T, k, E, d, dtype):
     say(f"permute/unpermute T={T} k={k} E={E} d={d} {dtype}")
