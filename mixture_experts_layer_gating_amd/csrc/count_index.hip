@@ -9,7 +9,8 @@
 // makes the result unique and deterministic.  No global atomics are used;
 // ranks come from wavefront ballots and LDS-staged scans.
 //
-// Three launches:
+// Three launches (two when the histogram table is small, see
+// ci_scan_scatter_kernel: each scatter block then does its own scan):
 //   1. count:   block b histograms its chunk of slots in LDS
 //               -> blk_cnt[e][b]                                  (workspace)
 //   2. scan:    one block: totals -> counts, offsets; per expert an exclusive
@@ -134,10 +135,13 @@ __device__ __forceinline__ uint64_t match_mask(int id, bool valid, int nbits) {
   return valid ? m : 0ull;
 }
 
-__global__ __launch_bounds__(kCiBlock) void ci_scatter_kernel(
-    const int32_t* __restrict__ ids, int Tk, int E, int nbits, int nblk,
-    const int32_t* __restrict__ blk_off, int32_t* __restrict__ dest, int32_t* __restrict__ src) {
-  extern __shared__ int32_t run[];  // [kCiWaves][E]
+// Ranks of block blockIdx.x's slots.  `first(e)` is the first row of this
+// block's slots of expert e; run is LDS of kCiWaves * E ints.
+template <class First>
+__device__ __forceinline__ void scatter_block(const int32_t* __restrict__ ids, int Tk, int E,
+                                              int nbits, First first, int32_t* run,
+                                              int32_t* __restrict__ dest,
+                                              int32_t* __restrict__ src) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
   for (int i = threadIdx.x; i < kCiWaves * E; i += kCiBlock) run[i] = 0;
@@ -158,7 +162,7 @@ __global__ __launch_bounds__(kCiBlock) void ci_scatter_kernel(
   __syncthreads();
   // Exclusive scan over waves, seeded with the block's first row per expert.
   for (int e = threadIdx.x; e < E; e += kCiBlock) {
-    int acc = blk_off[static_cast<size_t>(e) * nblk + blockIdx.x];
+    int acc = first(e);
     for (int w = 0; w < kCiWaves; ++w) {
       const int c = run[w * E + e];
       run[w * E + e] = acc;
@@ -183,6 +187,87 @@ __global__ __launch_bounds__(kCiBlock) void ci_scatter_kernel(
     }
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+__global__ __launch_bounds__(kCiBlock) void ci_scatter_kernel(
+    const int32_t* __restrict__ ids, int Tk, int E, int nbits, int nblk,
+    const int32_t* __restrict__ blk_off, int32_t* __restrict__ dest, int32_t* __restrict__ src) {
+  extern __shared__ int32_t run[];  // [kCiWaves][E]
+  scatter_block(ids, Tk, E, nbits,
+                [&](int e) { return blk_off[static_cast<size_t>(e) * nblk + blockIdx.x]; }, run,
+                dest, src);
+}
+
+// Scan and scatter in one launch, for small histogram tables (E <= 256 and
+// E * nblk <= kFusedTable): every block sums the block histograms itself --
+// all blocks before it, and all blocks for the totals -- so no separate
+// single-block scan is launched.  Block 0 also writes counts and offsets.
+// Same arithmetic as ci_scan_kernel (integer sums), so the same result.
+constexpr int kFusedExperts = 256;
+constexpr int kFusedTable = 16384;  // ints of blk_cnt read by every block
+
+__global__ __launch_bounds__(kCiBlock) void ci_scan_scatter_kernel(
+    const int32_t* __restrict__ ids, int Tk, int E, int nbits, int nblk,
+    const int32_t* __restrict__ blk_cnt, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ dest, int32_t* __restrict__ src) {
+  __shared__ int32_t before_s[kFusedExperts];
+  __shared__ int32_t base_s[kFusedExperts];
+  __shared__ int32_t run[kCiWaves * kFusedExperts];
+  const int lane = threadIdx.x & (kWave - 1);
+  // tpe threads per expert, a power of two <= 64 with E * tpe <= kCiBlock,
+  // so an expert's threads share a wave.
+  int tpe = 1;
+  while (tpe < kWave && 2 * tpe * E <= kCiBlock) tpe *= 2;
+  const int per_t = (nblk + tpe - 1) / tpe;
+  const int e = threadIdx.x / tpe, sub = threadIdx.x % tpe;
+  const bool act = e < E;
+  const int b0 = min(nblk, sub * per_t), b1 = min(nblk, b0 + per_t);
+  const int32_t* row = blk_cnt + static_cast<size_t>(act ? e : 0) * nblk;
+  const int me = static_cast<int>(blockIdx.x);
+  int before = 0, total = 0;
+  if (act) {
+    constexpr int kBatch = 8;  // loads in flight together
+    for (int b = b0; b < b1; b += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) v[q] = b + q < b1 ? row[b + q] : 0;
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        total += v[q];
+        before += b + q < me ? v[q] : 0;
+      }
+    }
+  }
+  // Sum over the expert's tpe threads (contiguous lanes of one wave).
+  for (int o = tpe / 2; o > 0; o >>= 1) {
+    total += __shfl_xor(total, o, kWave);
+    before += __shfl_xor(before, o, kWave);
+  }
+  if (act && sub == 0) {
+    base_s[e] = total;  // the totals first; the scan below turns them into offsets
+    before_s[e] = before;
+  }
+  __syncthreads();
+  // Exclusive scan of the totals over experts (wave 0).
+  if (threadIdx.x < kWave) {
+    int carry = 0;
+    for (int c = 0; c < E; c += kWave) {
+      const int v = c + lane < E ? base_s[c + lane] : 0;
+      const int iv = wave_inclusive_scan(v, lane);
+      if (c + lane < E) {
+        base_s[c + lane] = carry + iv - v;
+        if (me == 0) {
+          counts[c + lane] = v;
+          offsets[c + lane] = carry + iv - v;
+        }
+      }
+      carry += __shfl(iv, kWave - 1, kWave);
+    }
+    if (me == 0 && lane == 0) offsets[E] = carry;
+  }
+  __syncthreads();
+  scatter_block(ids, Tk, E, nbits, [&](int x) { return base_s[x] + before_s[x]; }, run, dest,
+                src);
 }
 
 int id_bits(int E) {
@@ -230,6 +315,12 @@ extern "C" moe_status moe_count_index(const int32_t* topk_idx, int T, int k, int
   hipLaunchKernelGGL(ci_count_kernel, dim3(nblk), dim3(kCiBlock), E * sizeof(int32_t), st,
                      topk_idx, static_cast<int>(Tk), E, nblk, blk_cnt);
   if (moe_status s = check_launch("moe_count_index/count")) return s;
+  if (E <= kFusedExperts && static_cast<long long>(E) * nblk <= kFusedTable) {
+    hipLaunchKernelGGL(ci_scan_scatter_kernel, dim3(nblk), dim3(kCiBlock), 0, st, topk_idx,
+                       static_cast<int>(Tk), E, id_bits(E), nblk, blk_cnt, counts, offsets, dest,
+                       src);
+    return check_launch("moe_count_index/scan+scatter");
+  }
   hipLaunchKernelGGL(ci_scan_kernel, dim3(1), dim3(kScanBlock), 0, st, blk_cnt, E, nblk, blk_off,
                      counts, offsets);
   if (moe_status s = check_launch("moe_count_index/scan")) return s;
