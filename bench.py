@@ -256,6 +256,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--overlap-wgrad", action="store_true",
                     help="expert weight-gradient GEMMs on a second stream")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the step captured as a HIP graph (per-kernel "
+                         "figures still come from eager steps)")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="write a text summary of a rocprofv3 --kernel-trace --stats output")
@@ -369,11 +372,23 @@ def main():
 
     log(f"[bench] timing {args.steps} steps (events on {', '.join(dom_calls)})")
     timed = Recorder(set(dom_calls))
-    layer.timer = timed.span
+    graph = None
+    if args.graph:
+        # The whole step as one HIP graph over the same input buffers (no
+        # events inside it: the dominant kernel is then timed in the
+        # breakdown pass below).
+        graph = layer.capture(x, wr, w1, w2, dy, bias=bias, forced_idx=forced)
+        for _ in range(max(1, args.warmup)):
+            graph.replay()
+    else:
+        layer.timer = timed.span
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     layer.timer = None
@@ -384,9 +399,16 @@ def main():
     # roof its algorithmic intensity falls under: MFMA above the ridge point
     # (peak FLOP/s over peak bytes/s, ~312 FLOP/B), HBM below it (tiny
     # groups, where the GEMMs stream weights and weight gradients).
-    dom_ms = timed.per_call_ms()
+    dom_ms = timed.per_call_ms() if graph is None else None
     flops_per_launch = sum(work[n][0] for n in dom_calls) / len(dom_calls)
     bytes_per_launch = sum(work[n][1] for n in dom_calls) / len(dom_calls)
+    if dom_ms is None:  # graph mode: one eager step with events on the dominant calls
+        probe = Recorder(set(dom_calls))
+        layer.timer = probe.span
+        step()
+        torch.cuda.synchronize()
+        layer.timer = None
+        dom_ms = probe.per_call_ms()
     avg_launch_ms = sum(dom_ms[n] for n in dom_calls) / len(dom_calls)
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     if flops_per_launch / bytes_per_launch >= ridge:
@@ -470,7 +492,8 @@ def main():
                                f"SwiGLU d_ff={wl.F}, fwd+bwd",
                    "T": wl.T, "d_model": wl.d, "experts": wl.E, "top_k": wl.k, "d_ff": wl.F,
                    "regime": wl.regime, "parallelism": "single GPU",
-                   "streams": 2 if args.overlap_wgrad else 1},
+                   "streams": 2 if args.overlap_wgrad else 1,
+                   "launch": "hip graph replay" if args.graph else "eager"},
         "grouped_gemm_frac_of_bf16_peak": round(gemm_frac, 4),
         "grouped_gemm_tflops": round(g_fl / (g_ms * 1e-3) / 1e12, 1),
         "roofline": roofline,

@@ -169,6 +169,35 @@ class MoELayer:
         self._inputs = (x, wr, w1, w2)
         return self.y
 
+    def capture(self, x, wr, w1, w2, dy, bias=None, forced_idx=None):
+        """Record one forward + backward over these input buffers as a HIP
+        graph and return it (a ``torch.cuda.CUDAGraph``): ``replay()`` re-runs
+        the whole step with no per-kernel launch cost on the host.
+
+        The graph holds the buffers' addresses, so inputs are updated in
+        place between replays; results land in the layer's buffers as after
+        :meth:`forward` and :meth:`backward`.  The library only enqueues
+        kernels (no allocation, no memset, no host synchronisation) and this
+        layer's buffers exist already, so every call of the step is
+        captured.  Single-stream order only (``overlap_wgrad=False``).
+        """
+        if self.overlap_wgrad:
+            raise ValueError("capture() records the single-stream order (overlap_wgrad=False)")
+        if self.timer is not None:
+            raise ValueError("capture() with a timer attached")
+        main = torch.cuda.current_stream(self.device)
+        side = torch.cuda.Stream(device=self.device)
+        side.wait_stream(main)
+        with torch.cuda.stream(side):  # one eager step off the capture
+            self.forward(x, wr, w1, w2, bias=bias, forced_idx=forced_idx)
+            self.backward(dy)
+        main.wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.forward(x, wr, w1, w2, bias=bias, forced_idx=forced_idx)
+            self.backward(dy)
+        return graph
+
     def _dw1(self, x, w1, ws, wsb, stream):
         """dW1 = xp^T @ dh, with xp read from x through src / k when gathering."""
         T, d, E, k, F, Tk, c = self.T, self.d, self.E, self.k, self.F, self.Tk, self.code

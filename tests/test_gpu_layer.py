@@ -115,6 +115,46 @@ def test_layer_deterministic():
         assert torch.equal(a, b)
 
 
+def test_layer_graph_replay():
+    """The step captured as a HIP graph: every replay gives the bits of an
+    eager step on the same inputs, also after the inputs are rewritten in
+    place and with eager steps between replays."""
+    from mixture_experts_layer_gating_amd.layer import MoELayer
+    wl = Workload("graph", T=1024, d=512, E=16, k=4, F=256, dtype="bf16", w_std=0.05, seed=21)
+    say("layer graph capture and replay")
+    bf = torch.bfloat16
+    inp_a = make_inputs(wl)
+    inp_b = make_inputs(wl.with_(seed=22))
+    a = [dev(t, bf) for t in (inp_a.x, inp_a.wr, inp_a.w1, inp_a.w2, inp_a.dy)]
+    b = [dev(t, bf) for t in (inp_b.x, inp_b.wr, inp_b.w1, inp_b.w2, inp_b.dy)]
+    layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, dtype=bf, device=DEV)
+
+    def outs():
+        g = Grads_of(layer)
+        return [t.clone() for t in (layer.idx, layer.dest, layer.y) + g]
+
+    def Grads_of(lay):
+        return (lay.dx, lay.dwr, lay.dw1, lay.dw2)
+
+    def eager(inp):
+        layer.forward(*inp[:4])
+        layer.backward(inp[4])
+        torch.cuda.synchronize()
+        return outs()
+
+    want_a, want_b = eager(a), eager(b)
+    bufs = [t.clone() for t in a]
+    graph = layer.capture(*bufs)
+    for want, src in ((want_a, a), (want_b, b), (want_b, b), (want_a, a)):
+        for buf, t in zip(bufs, src):
+            buf.copy_(t)
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, w in zip(outs(), want):
+            assert torch.equal(got, w)
+        eager(b)  # eager work between replays
+
+
 # ------------------------------------------------------------------ full-size workloads
 FULL = ["olmoe", "olmoe_skew", "olmoe_uniform", "sparse", "large"]
 
