@@ -76,6 +76,7 @@ SMALL = [
     dict(T=256, d=256, E=64, k=8, F=128),     # small groups, empty experts
     dict(T=1, d=64, E=4, k=4, F=32),          # one token, every expert selected (k = E)
     dict(T=37, d=72, E=5, k=1, F=40),         # top-1, widths not multiples of 64
+    dict(T=96, d=64, E=1024, k=32, F=32),     # the largest E and k the library takes
 ]
 
 
