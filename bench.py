@@ -424,6 +424,31 @@ def main():
                      "flops_per_launch": flops_per_launch, "bytes_per_launch": bytes_per_launch,
                      "avg_launch_ms": round(avg_launch_ms, 4)})
 
+    # Per-step medians (HIP events around each step): steps back to back,
+    # and steps each preceded by a 1 GiB write that flushes L2 and the MALL.
+    def step_medians(n, flush):
+        buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if flush else None
+        times = []
+        for _ in range(n):
+            if buf is not None:
+                buf.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if graph is not None:
+                graph.replay()
+            else:
+                step()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        del buf
+        times.sort()
+        return round(times[len(times) // 2], 4)
+
+    n_med = min(args.steps, 10)
+    step_median = {"warm_ms": step_medians(n_med, False),
+                   "after_cache_flush_ms": step_medians(n_med, True), "steps": n_med}
+
     # Per-call breakdown: a separate pass after the timed region, every call timed.
     n_brk = min(args.steps, 10)
     log(f"[bench] per-call breakdown over {n_brk} further steps")
@@ -497,6 +522,7 @@ def main():
         "grouped_gemm_frac_of_bf16_peak": round(gemm_frac, 4),
         "grouped_gemm_tflops": round(g_fl / (g_ms * 1e-3) / 1e12, 1),
         "roofline": roofline,
+        "step_median": step_median,
         "library_gemm_reference": ref_gemm,
         "kernels": kernels,
         "kernels_note": f"per-call times from {n_brk} steps after the timed region",
