@@ -703,12 +703,17 @@ __device__ __forceinline__ void reduce_tile(f32x16 (&acc)[MI][NI], XL& xl, YL& y
   __builtin_amdgcn_s_barrier();
   Frags<MI, NI> f0, f1;
   read_frags<MIV, XS, YS>(f0, xb, yb, 0, 0, xa, ya);
-  for (int kt = 0; kt < nk; kt += 4) {
+  // Four steps per iteration; the last iteration, when the reduction is
+  // not a multiple of four steps, runs as a separate copy that leaves out
+  // the MFMAs of the steps past the end (their operands are zeros), so the
+  // full iterations keep their fixed schedule.
+  auto four_steps = [&](int kt, auto guarded) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      const bool live = !decltype(guarded)::value || kt + s < nk;
       xl.prepare(s);  // gathered x: rows of the call this step issues
       read_frags<MIV, XS, YS>(f1, xb, yb, s, 1, xa, ya);
-      mfma_step<MIV>(acc, f0);
+      if (live) mfma_step<MIV>(acc, f0);
       interleave_mfma_ds<MIV * NI>();
       __builtin_amdgcn_sched_barrier(0);
       // Issued after the loads step s + 1 needs: steps s + 2 and s + 3, minus
@@ -720,11 +725,14 @@ __device__ __forceinline__ void reduce_tile(f32x16 (&acc)[MI][NI], XL& xl, YL& y
       __builtin_amdgcn_s_barrier();
       issue_step<XS, YS>(xl, yl, xb, yb, s, kt + s + 4);
       read_frags<MIV, XS, YS>(f0, xb, yb, s + 1, 0, xa, ya);
-      mfma_step<MIV>(acc, f1);
+      if (live) mfma_step<MIV>(acc, f1);
       interleave_mfma_ds<MIV * NI>();
       __builtin_amdgcn_sched_barrier(0);
     }
-  }
+  };
+  int kt = 0;
+  for (; kt + 4 <= nk; kt += 4) four_steps(kt, std::false_type{});
+  if (kt < nk) four_steps(kt, std::true_type{});
   // Drain the loads of the last steps before the workgroup's LDS is released.
   wait_vmcnt<0>();
 }
