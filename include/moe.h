@@ -36,8 +36,10 @@
  *   never reads device memory; on error nothing is enqueued and
  *   moe_last_error() returns a message (thread-local, valid until the next
  *   call on the same thread).  MOE_ERR_HIP reports a failed kernel launch.
- *   Out-of-range expert ids or row indices inside device buffers are caller
- *   bugs and give undefined results.
+ *   Out-of-range expert ids inside device buffers are caller bugs: the
+ *   routing and counting kernels clamp them into [0, E), so the results for
+ *   those slots are meaningless but every index derived from them stays a
+ *   valid row.  Row maps (dest, src) must come from moe_count_index.
  * - Weight layouts: router wr[d, E]; expert W1[E, d, 2F] (columns [0, F) gate,
  *   [F, 2F) up); expert W2[E, F, d].
  */
@@ -88,6 +90,10 @@ const char* moe_version(void);
  *   topk_idx [T, k] int32, out.         topk_w [T, k] float32, out.
  *   probs    [T, E] float32 or NULL, out (p, kept for the backward pass).
  * Requires 1 <= k <= min(E, 32), 1 <= E <= 1024, T >= 1.
+ * NaN scores rank below every number (-inf included) and among themselves by
+ * expert index, so every token gets k distinct ids in [0, E) even when its
+ * logits hold NaNs (the order of a stable descending sort with NaNs last);
+ * the weights of such a token are then NaN.
  */
 moe_status moe_route_topk(const float* logits, const float* bias, int T, int E,
                           int k, int renorm, const int32_t* forced_idx,
@@ -145,7 +151,12 @@ moe_status moe_permute(const void* x, const int32_t* dest, int T, int k, int d,
                        moe_dtype dtype, void* xp, moe_stream_t stream);
 
 /*
- * moe_unpermute -- weighted combine back to token order:
+ * moe_unpermute -- weighted combine back to token order [Summary, Method
+ * details / technical framework: experts are selected, then computed, and
+ * their outputs form the layer's output for each token; Brief, Core method:
+ * the expert computation runs on tokens grouped per expert, so the results
+ * return to token order].  No passage defines the combination; the reading
+ * used is the gate-weighted sum of the token's k expert outputs:
  * y[t, :] = sum_{j<k} w[t, j] * yp[dest[t*k + j], :], summed in float32 in
  * increasing j, rounded once to `dtype`.  With w == NULL every weight is 1
  * (this is also the backward pass of moe_permute).
@@ -157,7 +168,8 @@ moe_status moe_unpermute(const void* yp, const int32_t* dest, const float* w,
                          moe_stream_t stream);
 
 /*
- * moe_unpermute_bwd -- backward of moe_unpermute:
+ * moe_unpermute_bwd -- backward of moe_unpermute [Brief, Key results: the
+ * sped-up unit is the forward plus the backward pass]:
  * dyp[dest[t*k+j], :] = w[t, j] * dy[t, :]   (rounded to dtype) and
  * dw[t, j] = sum_i dy[t, i] * yp[dest[t*k+j], i]   (float32).
  *   dy [T, d], yp [T*k, d], dyp [T*k, d]: `dtype`.  w [T, k] float32, in.

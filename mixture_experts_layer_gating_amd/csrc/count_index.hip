@@ -34,6 +34,15 @@ constexpr int kScanBlock = 1024;
 
 inline int num_chunks(long long Tk) { return static_cast<int>((Tk + kCiChunk - 1) / kCiChunk); }
 
+// Expert id of a slot.  Ids outside [0, E) are a caller error (the routing
+// kernel never writes one); they are clamped, so that counts still sum to
+// T*k, dest / src stay a permutation and every row index derived from them
+// stays inside its buffer.
+__device__ __forceinline__ int load_id(const int32_t* __restrict__ ids, int s, int E) {
+  const int id = ids[s];
+  return id < 0 ? 0 : (id >= E ? E - 1 : id);
+}
+
 __global__ __launch_bounds__(kCiBlock) void ci_count_kernel(const int32_t* __restrict__ ids,
                                                             int Tk, int E, int nblk,
                                                             int32_t* __restrict__ blk_cnt) {
@@ -42,7 +51,7 @@ __global__ __launch_bounds__(kCiBlock) void ci_count_kernel(const int32_t* __res
   __syncthreads();
   const int base = blockIdx.x * kCiChunk;
   const int end = min(base + kCiChunk, Tk);
-  for (int s = base + threadIdx.x; s < end; s += kCiBlock) atomicAdd(&hist[ids[s]], 1);
+  for (int s = base + threadIdx.x; s < end; s += kCiBlock) atomicAdd(&hist[load_id(ids, s, E)], 1);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kCiBlock)
     blk_cnt[static_cast<size_t>(e) * nblk + blockIdx.x] = hist[e];
@@ -155,7 +164,7 @@ __device__ __forceinline__ void scatter_block(const int32_t* __restrict__ ids, i
   for (int s0 = wbase; s0 < wend; s0 += kWave) {
     const int s = s0 + lane;
     const bool valid = s < wend;
-    const int id = valid ? ids[s] : 0;
+    const int id = valid ? load_id(ids, s, E) : 0;
     const uint64_t m = match_mask(id, valid, nbits);
     if (valid && (m & lt) == 0) myrun[id] += __popcll(m);
   }
@@ -174,7 +183,7 @@ __device__ __forceinline__ void scatter_block(const int32_t* __restrict__ ids, i
   for (int s0 = wbase; s0 < wend; s0 += kWave) {
     const int s = s0 + lane;
     const bool valid = s < wend;
-    const int id = valid ? ids[s] : 0;
+    const int id = valid ? load_id(ids, s, E) : 0;
     const uint64_t m = match_mask(id, valid, nbits);
     int row = 0;
     if (valid) row = myrun[id] + __popcll(m & lt);

@@ -24,9 +24,24 @@ namespace {
 
 constexpr int kRouteBlock = 256;  // 4 tokens per block
 
-// Order used for selection: larger value first, then lower index.
+// Order used for selection: larger value first, then lower index.  A NaN
+// ranks below every number (-inf included) and NaNs among themselves by
+// index, so a token whose logits hold NaNs still gets k distinct ids in
+// [0, E) -- the order of a stable descending sort that puts NaNs last.
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+  const bool na = va != va, nb = vb != vb;
+  if (na || nb) return nb && (!na || ia < ib);
   return (va > vb) || (va == vb && ia < ib);
+}
+
+// Start of an arg-max: worse than every candidate (NaN, with an index above
+// any expert's).
+constexpr int kNoExpert = 0x7fffffff;
+
+// A forced expert id outside [0, E) is a caller error; it is clamped so that
+// no read or row index derived from it leaves its buffer.
+__device__ __forceinline__ int clamp_expert(int e, int E) {
+  return e < 0 ? 0 : (e >= E ? E - 1 : e);
 }
 
 template <int EPL>
@@ -78,7 +93,7 @@ __global__ __launch_bounds__(kRouteBlock) void route_topk_kernel(
   float my_p = 0.f;
   if (forced) {
     if (lane < k) {
-      const int e = forced[static_cast<size_t>(t) * k + lane];
+      const int e = clamp_expert(forced[static_cast<size_t>(t) * k + lane], E);
       float v = row[e];
       if (bias) v = v + bias[e];
       my_id = e;
@@ -87,8 +102,8 @@ __global__ __launch_bounds__(kRouteBlock) void route_topk_kernel(
   } else {
     uint32_t taken = 0;  // bit i: register slot i already selected
     for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
+      float bv = __builtin_nanf("");
+      int bi = kNoExpert;
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
         const int e = i * kWave + lane;
@@ -191,7 +206,7 @@ __global__ __launch_bounds__(kRouteBlock) void route_topk_small_kernel(
     for (int q = 0; q < kSlots; ++q) {
       const int j = q * kGroup + g;
       if (j < k) {
-        const int e = forced[static_cast<size_t>(t) * k + j];
+        const int e = clamp_expert(forced[static_cast<size_t>(t) * k + j], E);
         float x = row[e];
         if (bias) x = x + bias[e];
         my_id[q] = e;
@@ -201,8 +216,8 @@ __global__ __launch_bounds__(kRouteBlock) void route_topk_small_kernel(
   } else {
     uint32_t taken = 0;  // bit v: register v already selected
     for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
+      float bv = __builtin_nanf("");
+      int bi = kNoExpert;
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         const int e = g * V + v;

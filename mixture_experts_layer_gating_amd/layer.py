@@ -72,6 +72,8 @@ class MoELayer:
         plan = L.moe_grouped_gemm_plan(3, T * k, d, 2 * F, E, self.code)
         self.gather_x = bool(gather_x) and self.fuse_act and bool(plan["mfma"])
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         Tk = T * k
         self.Tk = Tk
         dev = self.device
@@ -88,8 +90,9 @@ class MoELayer:
         self.router_offsets = torch.tensor([0, T], dtype=i32, device=dev)
         ci_ws = L.moe_count_index_workspace_size(T, k, E)
         self.ci_ws = torch.empty(max(ci_ws, 16), dtype=torch.uint8, device=dev)
-        # expert activations (expert-sorted rows)
-        self.xp = torch.empty(Tk, d, dtype=dtype, device=dev)
+        # expert activations (expert-sorted rows); the permuted copy of x
+        # exists only when GEMM 1 does not gather x through src / k
+        self.xp = None if self.gather_x else torch.empty(Tk, d, dtype=dtype, device=dev)
         self.h = torch.empty(Tk, 2 * F, dtype=dtype, device=dev)
         self.a = torch.empty(Tk, F, dtype=dtype, device=dev)
         self.yp = torch.empty(Tk, d, dtype=dtype, device=dev)
@@ -131,9 +134,28 @@ class MoELayer:
     def _span(self, name):
         return self.timer(name) if self.timer is not None else contextlib.nullcontext()
 
+    def _expect(self, t, name, shape, dtype):
+        """The kernels size their buffer ranges from (T, d, E, k, F), not from
+        the tensors: a tensor of another shape, dtype or device would be read
+        past its end, so it is refused here."""
+        if t is None:
+            return
+        if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != self.device:
+            raise ValueError(f"{name}: expected {tuple(shape)} {dtype} on {self.device}, got "
+                             f"{tuple(t.shape)} {t.dtype} on {t.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: must be contiguous")
+
     # ------------------------------------------------------------------
     def forward(self, x, wr, w1, w2, bias=None, forced_idx=None, stream=None):
         T, d, E, k, F, Tk, c = self.T, self.d, self.E, self.k, self.F, self.Tk, self.code
+        for t, name, shape in ((x, "x", (T, d)), (wr, "wr", (d, E)), (w1, "w1", (E, d, 2 * F)),
+                               (w2, "w2", (E, F, d))):
+            if t is None:
+                raise ValueError(f"{name} is required")
+            self._expect(t, name, shape, self.dtype)
+        self._expect(bias, "bias", (E,), torch.float32)
+        self._expect(forced_idx, "forced_idx", (T, k), torch.int32)
         s = stream
         with self._span("router_fwd"):
             L.moe_grouped_gemm_fwd(x, wr, self.router_offsets, T, d, E, 1, c, self.logits,
@@ -214,6 +236,9 @@ class MoELayer:
             raise RuntimeError("backward() before forward()")
         x, wr, w1, w2 = self._inputs
         T, d, E, k, F, Tk, c = self.T, self.d, self.E, self.k, self.F, self.Tk, self.code
+        if dy is None:
+            raise ValueError("dy is required")
+        self._expect(dy, "dy", (T, d), self.dtype)
         s = stream
         ws, wsb = self.gemm_ws, self.gemm_ws_bytes
         overlap = self.overlap_wgrad and (s is None or isinstance(s, torch.cuda.Stream))
@@ -248,7 +273,8 @@ class MoELayer:
                 L.moe_grouped_gemm_bwd(self.a, w2, self.dyp, self.offsets, Tk, F, d, E, c, None,
                                        None, self.dw2, ws, wsb, stream=main)
         with self._span("gemm1_bwd_da"):
-            L.moe_grouped_gemm_bwd(self.xp, w1, self.dh, self.offsets, Tk, d, 2 * F, E, c,
+            # data gradient only: the activation operand `a` is not read
+            L.moe_grouped_gemm_bwd(None, w1, self.dh, self.offsets, Tk, d, 2 * F, E, c,
                                    self.dxp, None, None, ws, wsb, stream=main)
         with self._span("permute_bwd"):
             L.moe_unpermute(self.dxp, self.dest, None, T, k, d, c, self.dx_e, stream=main)

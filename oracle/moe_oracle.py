@@ -56,9 +56,30 @@ finite differences of the forward pass.
 """
 from __future__ import annotations
 
+import contextlib
+
 import numpy as np
 
 F64 = np.float64
+# Working precision of every step: float64, the precision the oracle is
+# pinned and compared in.  ``precision`` switches it (float32 for the CPU
+# throughput baseline) without changing any definition.
+FT = np.float64
+
+
+@contextlib.contextmanager
+def precision(dtype):
+    """Evaluate the oracle's steps in ``dtype`` (e.g. ``np.float32``) inside
+    the block.  Only the dtype of the arrays changes; the definitions, the
+    order of the steps and the library routines are the same.  Not
+    thread-safe (module state)."""
+    global FT
+    old = FT
+    FT = np.dtype(dtype).type
+    try:
+        yield
+    finally:
+        FT = old
 
 
 # --------------------------------------------------------------------------
@@ -66,7 +87,7 @@ F64 = np.float64
 # --------------------------------------------------------------------------
 def router_logits(x, wr):
     """Router logits ``L[t, e] = sum_i x[t, i] * wr[i, e]`` in float64."""
-    return np.asarray(x, F64) @ np.asarray(wr, F64)
+    return np.asarray(x, FT) @ np.asarray(wr, FT)
 
 
 def biased_logits(logits, bias):
@@ -87,7 +108,7 @@ def softmax(z):
 
     The row maximum is subtracted first; this leaves the value unchanged.
     """
-    z = np.asarray(z, F64)
+    z = np.asarray(z, FT)
     m = z.max(axis=-1, keepdims=True)
     ez = np.exp(z - m)
     return ez / ez.sum(axis=-1, keepdims=True)
@@ -108,7 +129,7 @@ def topk_experts(z, k):
 def gate_weights(p, idx, renorm=False):
     """Combine weights ``w[t, j] = p[t, idx[t, j]]`` (R1), optionally divided
     by their sum over j."""
-    w = np.take_along_axis(np.asarray(p, F64), np.asarray(idx, np.int64), axis=1)
+    w = np.take_along_axis(np.asarray(p, FT), np.asarray(idx, np.int64), axis=1)
     if renorm:
         w = w / w.sum(axis=1, keepdims=True)
     return w
@@ -178,43 +199,43 @@ def grouped_matmul(a, w, offsets):
     ``a[M, K]`` expert-sorted rows, ``w[E, K, N]``; returns ``c[M, N]`` with
     ``c[offsets[e]:offsets[e+1]] = a[offsets[e]:offsets[e+1]] @ w[e]``.
     """
-    a = np.asarray(a, F64)
+    a = np.asarray(a, FT)
     E, K, N = w.shape
-    c = np.zeros((a.shape[0], N), dtype=F64)
+    c = np.zeros((a.shape[0], N), dtype=FT)
     for e in range(E):
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
         if r1 > r0:
-            c[r0:r1] = a[r0:r1] @ np.asarray(w[e], F64)
+            c[r0:r1] = a[r0:r1] @ np.asarray(w[e], FT)
     return c
 
 
 def sigmoid(z):
     """Logistic function 1 / (1 + exp(-z)), overflow-free form."""
-    z = np.asarray(z, F64)
+    z = np.asarray(z, FT)
     return np.exp(-np.logaddexp(0.0, -z))
 
 
 def silu(z):
     """SiLU (swish) ``z * sigmoid(z)``."""
-    z = np.asarray(z, F64)
+    z = np.asarray(z, FT)
     return z * sigmoid(z)
 
 
 def swiglu(h):
     """Gated activation of R7: ``A = silu(G) * U`` with ``G, U = h[:, :F],
     h[:, F:]``."""
-    h = np.asarray(h, F64)
+    h = np.asarray(h, FT)
     F = h.shape[1] // 2
     return silu(h[:, :F]) * h[:, F:]
 
 
 def combine(yp, dest, w, k):
     """Weighted un-permute (R8): ``y[t] = sum_j w[t, j] * yp[dest[t*k + j]]``."""
-    yp = np.asarray(yp, F64)
-    w = np.asarray(w, F64)
+    yp = np.asarray(yp, FT)
+    w = np.asarray(w, FT)
     T = w.shape[0]
     d2 = np.asarray(dest).reshape(T, k)
-    y = np.zeros((T, yp.shape[1]), dtype=F64)
+    y = np.zeros((T, yp.shape[1]), dtype=FT)
     for j in range(k):
         y += w[:, j:j + 1] * yp[d2[:, j]]
     return y
@@ -228,7 +249,7 @@ def layer_forward(x, wr, w1, w2, k, bias=None, forced_idx=None, renorm=False,
     the routing decision on exactly those values; otherwise they are
     ``x @ wr`` in float64.
     """
-    x = np.asarray(x, F64)
+    x = np.asarray(x, FT)
     T = x.shape[0]
     E = w1.shape[0]
     if logits is None:
@@ -252,13 +273,13 @@ def layer_forward(x, wr, w1, w2, k, bias=None, forced_idx=None, renorm=False,
 def combine_backward(dy, yp, dest, w, k):
     """Gradients of R8: ``dyp[dest[t*k+j]] = w[t, j] * dy[t]`` and
     ``dw[t, j] = <dy[t], yp[dest[t*k+j]]>``."""
-    dy = np.asarray(dy, F64)
-    yp = np.asarray(yp, F64)
-    w = np.asarray(w, F64)
+    dy = np.asarray(dy, FT)
+    yp = np.asarray(yp, FT)
+    w = np.asarray(w, FT)
     T = dy.shape[0]
     d2 = np.asarray(dest).reshape(T, k)
     dyp = np.zeros_like(yp)
-    dw = np.zeros((T, k), dtype=F64)
+    dw = np.zeros((T, k), dtype=FT)
     for j in range(k):
         dyp[d2[:, j]] = w[:, j:j + 1] * dy
         dw[:, j] = np.sum(dy * yp[d2[:, j]], axis=1)
@@ -269,15 +290,15 @@ def grouped_matmul_backward(a, w, dc, offsets):
     """Gradients of ``grouped_matmul``: per expert e,
     ``da_e = dc_e @ w[e]^T`` and ``dw[e] = a_e^T @ dc_e`` (zero for an expert
     with no rows)."""
-    a = np.asarray(a, F64)
-    dc = np.asarray(dc, F64)
+    a = np.asarray(a, FT)
+    dc = np.asarray(dc, FT)
     E, K, N = w.shape
-    da = np.zeros((a.shape[0], K), dtype=F64)
-    dw = np.zeros((E, K, N), dtype=F64)
+    da = np.zeros((a.shape[0], K), dtype=FT)
+    dw = np.zeros((E, K, N), dtype=FT)
     for e in range(E):
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
         if r1 > r0:
-            we = np.asarray(w[e], F64)
+            we = np.asarray(w[e], FT)
             da[r0:r1] = dc[r0:r1] @ we.T
             dw[e] = a[r0:r1].T @ dc[r0:r1]
     return da, dw
@@ -286,8 +307,8 @@ def grouped_matmul_backward(a, w, dc, offsets):
 def swiglu_backward(h, da):
     """Gradient of ``swiglu``: with s = sigmoid(G),
     ``dG = da * U * s * (1 + G * (1 - s))`` and ``dU = da * G * s``."""
-    h = np.asarray(h, F64)
-    da = np.asarray(da, F64)
+    h = np.asarray(h, FT)
+    da = np.asarray(da, FT)
     F = h.shape[1] // 2
     g, u = h[:, :F], h[:, F:]
     s = sigmoid(g)
@@ -298,9 +319,9 @@ def swiglu_backward(h, da):
 
 def permute_backward(dxp, dest, k, T):
     """Gradient of ``permute``: ``dx[t] = sum_j dxp[dest[t*k + j]]``."""
-    dxp = np.asarray(dxp, F64)
+    dxp = np.asarray(dxp, FT)
     d2 = np.asarray(dest).reshape(T, k)
-    dx = np.zeros((T, dxp.shape[1]), dtype=F64)
+    dx = np.zeros((T, dxp.shape[1]), dtype=FT)
     for j in range(k):
         dx += dxp[d2[:, j]]
     return dx
@@ -314,8 +335,8 @@ def gate_backward(p, idx, dw, renorm=False):
     ``dp_j = (dw_j - sum_l dw_l w_l) / S``), scattered into ``dp[T, E]``;
     then the softmax Jacobian: ``dz = p * (dp - <p, dp>)``.
     """
-    p = np.asarray(p, F64)
-    dw = np.asarray(dw, F64)
+    p = np.asarray(p, FT)
+    dw = np.asarray(dw, FT)
     idx = np.asarray(idx, np.int64)
     T, E = p.shape
     if renorm:
@@ -325,7 +346,7 @@ def gate_backward(p, idx, dw, renorm=False):
         dpk = (dw - np.sum(dw * wn, axis=1, keepdims=True)) / S
     else:
         dpk = dw
-    dp = np.zeros((T, E), dtype=F64)
+    dp = np.zeros((T, E), dtype=FT)
     rows = np.repeat(np.arange(T), idx.shape[1])
     np.add.at(dp, (rows, idx.reshape(-1)), dpk.reshape(-1))
     return p * (dp - np.sum(p * dp, axis=1, keepdims=True))
@@ -333,9 +354,9 @@ def gate_backward(p, idx, dw, renorm=False):
 
 def router_backward(x, wr, dz):
     """Gradients of ``router_logits``: ``dx = dz @ wr^T``, ``dwr = x^T @ dz``."""
-    x = np.asarray(x, F64)
-    wr = np.asarray(wr, F64)
-    dz = np.asarray(dz, F64)
+    x = np.asarray(x, FT)
+    wr = np.asarray(wr, FT)
+    dz = np.asarray(dz, FT)
     return dz @ wr.T, x.T @ dz
 
 
@@ -345,7 +366,7 @@ def layer_backward(fwd, dy, x, wr, w1, w2, k, renorm=False):
     Returns a dict with ``dx``, ``dwr``, ``dw1``, ``dw2`` and the
     intermediates ``dyp, dw, da, dh, dxp, dz``.
     """
-    dy = np.asarray(dy, F64)
+    dy = np.asarray(dy, FT)
     T = dy.shape[0]
     dyp, dw = combine_backward(dy, fwd["yp"], fwd["dest"], fwd["w"], k)
     da, dw2 = grouped_matmul_backward(fwd["a"], w2, dyp, fwd["offsets"])

@@ -19,6 +19,13 @@ TOL_F32 = 1e-5    # float32 path, and every float32 gate weight / probability
 # accurate to ~1e-6 has per-element relative error <= 2^-9 ~ 1.95e-3, so its
 # relative Frobenius error is below that; 2.5e-3 leaves room for the fp32 part.
 TOL_ONE_ROUNDING = 2.5e-3
+# Router logits: float32 sums of exactly representable products (bf16 x bf16,
+# or float32 inputs), so their only error is float32 accumulation rounding
+# (~sqrt(#terms) * 2^-24 relative to the partial sums: ~1e-6 at d = 4096).
+TOL_LOGITS = 1e-5
+# A routing difference counts as a near tie when the picked expert's score is
+# within this fraction of the token's largest |score| of the score it replaces.
+NEAR_TIE = 1e-5
 
 
 def say(*a):
@@ -56,37 +63,37 @@ def rel(got, ref):
     return O.rel_fro(got, ref)
 
 
-# ------------------------------------------------------------------ sampling
-def sample_tokens(inp, gpu_logits, k, tokens, renorm=False):
-    """Oracle forward+backward of the given tokens only (tokens are
-    independent in the forward pass and in dx), routed on the device's fp32
-    logits of those tokens.  Returns (fwd, bwd) dicts of the sub-problem:
-    y, dx, dz (= dlogits), w, idx are exact for these tokens."""
-    t = np.asarray(tokens)
-    forced = None if inp.forced_idx is None else inp.forced_idx[t]
-    fwd = O.layer_forward(inp.x[t], inp.wr, inp.w1, inp.w2, k, bias=inp.bias, forced_idx=forced,
-                          renorm=renorm, logits=gpu_logits[t])
-    bwd = O.layer_backward(fwd, inp.dy[t], inp.x[t], inp.wr, inp.w1, inp.w2, k, renorm=renorm)
-    return fwd, bwd
+# ------------------------------------------------------------------ comparisons
+def routing_flips(idx, z, k):
+    """Tokens whose selected ids ``idx [T,k]`` differ from the oracle's top-k of
+    the float64 scores ``z [T,E]``, and those among them that are NOT near
+    ties.  A token is a near tie when its ids are distinct and, for every slot
+    j, the score (in ``z``) of its j-th id is within NEAR_TIE * max|z[t]| of
+    the j-th largest score: the two selections then differ only by the
+    rounding of scores that are equal to that accuracy."""
+    oi = O.topk_experts(z, k)
+    diff = np.flatnonzero((np.asarray(idx) != oi).any(axis=1))
+    bad = []
+    for t in diff:
+        zt = np.asarray(z[t], np.float64)
+        ranked = -np.sort(-zt)[:k]
+        eps = NEAR_TIE * np.max(np.abs(zt))
+        ids = np.asarray(idx[t])
+        if len(set(ids.tolist())) != k or np.any(np.abs(zt[ids] - ranked) > eps):
+            bad.append(int(t))
+    return diff, bad
 
 
-def expert_weight_grads(inp, k, idx, w, e):
-    """Oracle dW1[e], dW2[e] from every slot routed to expert e (routing
-    idx/w given), composed from the oracle's per-step functions on the
-    one-expert sub-problem."""
-    flat = idx.reshape(-1)
-    slots = np.flatnonzero(flat == e)
-    tok = slots // k
-    n = len(slots)
-    off = np.array([0, n])
-    w1 = inp.w1[e:e + 1]
-    w2 = inp.w2[e:e + 1]
-    xp = inp.x[tok].astype(np.float64)
-    wt = w.reshape(-1)[slots][:, None]
-    h = O.grouped_matmul(xp, w1, off)
-    a = O.swiglu(h)
-    dyp = wt * inp.dy[tok].astype(np.float64)
-    da, dw2 = O.grouped_matmul_backward(a, w2, dyp, off)
-    dh = O.swiglu_backward(h, da)
-    _, dw1 = O.grouped_matmul_backward(xp, w1, dh, off)
-    return dw1[0], dw2[0], n
+def rel_by_expert(dev_t, ref, cols=slice(None)):
+    """Relative Frobenius error of a device tensor ``[E, R, C]`` (any float
+    dtype) against ``ref`` over columns ``cols``, one expert at a time, so
+    that no float64 copy of the whole device tensor is made."""
+    num = den = 0.0
+    for e in range(ref.shape[0]):
+        g = host(dev_t[e])[:, cols]
+        r = np.asarray(ref[e], np.float64)[:, cols]
+        num += float(np.sum((g - r) ** 2))
+        den += float(np.sum(r ** 2))
+    if den == 0.0:
+        return 0.0 if num == 0.0 else float("inf")
+    return float(np.sqrt(num / den))

@@ -1,20 +1,20 @@
 """GPU parity of the whole layer (forward + backward through MoELayer, i.e.
 through the C ABI, in the launch configuration the benchmark times).
 
-Small shapes: every output compared in full against the oracle.  The five
-workload shapes at full size: routing / counts / indices compared in full
-(bit-exact), float outputs on sampled tokens and sampled experts that the
-oracle computes one by one.  The routing decision is taken on the device's
-float32 logits (the oracle's own float64 logits are compared separately), so
-near-ties cannot make the two sides route differently."""
+Small shapes and the five workload shapes at full size: every output compared
+in full against the oracle.  The router logits are held to the oracle's own
+float64 logits (1e-5), and routing flips against the oracle's routing on those
+logits are counted and must all be near ties; the routing decision compared
+bit-exactly is the oracle's on the device's float32 logits (the decision is
+taken in the logits' own precision)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
 from moe_inputs import WORKLOADS, Workload, make_inputs
-from tests._gpu import (DEV, TOL_BF16, TOL_F32, dev, expert_weight_grads, host, rel,
-                        sample_tokens, say)
+from tests._gpu import (DEV, TOL_BF16, TOL_F32, TOL_LOGITS, dev, host, rel, rel_by_expert,
+                        routing_flips, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,8 +44,13 @@ def _full_compare(inp, renorm=False):
     tol = TOL_BF16 if wl.dtype == "bf16" else TOL_F32
     layer, g, _ = _run(inp, renorm)
     logits = host(layer.logits).astype(np.float32)
-    # the device's logits agree with the oracle's own float64 logits
-    assert rel(logits, O.router_logits(inp.x, inp.wr)) <= tol
+    # the device's logits agree with the oracle's own float64 logits (float32
+    # sums of exactly representable products)
+    ologits = O.router_logits(inp.x, inp.wr)
+    assert rel(logits, ologits) <= TOL_LOGITS
+    if inp.forced_idx is None:
+        _, bad = routing_flips(host(layer.idx), O.biased_logits(ologits, inp.bias), wl.k)
+        assert not bad, f"tokens {bad[:8]} route differently without a near tie"
     fwd = O.layer_forward(inp.x, inp.wr, inp.w1, inp.w2, wl.k, bias=inp.bias,
                           forced_idx=inp.forced_idx, renorm=renorm, logits=logits)
     bwd = O.layer_backward(fwd, inp.dy, inp.x, inp.wr, inp.w1, inp.w2, wl.k, renorm=renorm)
@@ -160,53 +165,67 @@ def test_layer_graph_replay():
 FULL = ["olmoe", "olmoe_skew", "olmoe_uniform", "sparse", "large"]
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_layer_full_size_sampled(name):
+@pytest.mark.parametrize("name", [pytest.param(n, marks=pytest.mark.timeout(900)) for n in FULL])
+def test_layer_full_size(name):
+    """The five workload shapes at full size, every output compared in full
+    against one whole oracle pass:
+
+    * router logits against the oracle's own float64 logits (<= 1e-5);
+    * routing flips against the oracle's routing on those float64 logits:
+      every token whose ids differ must be a near tie (the device's j-th pick
+      holds, in the float64 scores, the j-th largest value within
+      1e-5 * max |score| of the token); the count is printed;
+    * ids, counts, offsets, dest, src bit-exact against the oracle's routing
+      on the device's float32 logits (the decision is taken in the logits'
+      own precision), gate weights <= 1e-5;
+    * y, dx, dlogits, the gate-weight gradient, dwr, every expert's dW1
+      (gate and up halves) and dW2 against the oracle pass routed on those
+      logits, <= 1e-2 (bf16 storage, float32 accumulation)."""
     wl = WORKLOADS[name]
     say(f"layer full size {wl}")
     inp = make_inputs(wl)
     layer, g, _ = _run(inp)
     say("  gpu done")
-    k = wl.k
+    k, E = wl.k, wl.E
     logits = host(layer.logits).astype(np.float32)
-    # routing, counts, indices: full and bit-exact (decision on device logits)
-    oidx, ow, op = O.route(logits, k, bias=inp.bias, forced_idx=inp.forced_idx)
-    np.testing.assert_array_equal(host(layer.idx), oidx)
-    assert rel(host(layer.w), ow) <= TOL_F32
-    counts, offsets, dest, src = O.build_index(oidx, wl.E)
-    for key, want in (("counts", counts), ("offsets", offsets), ("dest", dest), ("src", src)):
-        np.testing.assert_array_equal(host(getattr(layer, key)), want, err_msg=key)
+    # logits against the oracle's float64 logits
+    ologits = O.router_logits(inp.x, inp.wr)
+    errs = {"logits": rel(logits, ologits)}
+    assert errs["logits"] <= TOL_LOGITS, errs
+    idx = host(layer.idx)
+    if inp.forced_idx is None:
+        diff, bad = routing_flips(idx, O.biased_logits(ologits, inp.bias), k)
+        say(f"  routing flips against float64 logits: {len(diff)} tokens, "
+            f"{len(bad)} not near ties")
+        assert not bad, f"tokens {bad[:8]} route differently without a near tie"
+    else:
+        np.testing.assert_array_equal(idx, inp.forced_idx)
+    # the whole oracle pass, routed on the device's float32 logits
+    fwd = O.layer_forward(inp.x, inp.wr, inp.w1, inp.w2, k, bias=inp.bias,
+                          forced_idx=inp.forced_idx, logits=logits)
+    say("  oracle forward done")
+    for key in ("idx", "counts", "offsets", "dest", "src"):
+        np.testing.assert_array_equal(host(getattr(layer, key)).reshape(-1),
+                                      np.asarray(fwd[key]).reshape(-1), err_msg=key)
+    counts = fwd["counts"]
     if wl.regime == "uniform":
-        assert (counts == wl.Tk // wl.E).all()
+        assert (counts == wl.Tk // E).all()
     say(f"  routing ok; rows/expert min {counts.min()} max {counts.max()}")
-    # logits of sampled tokens against the oracle's float64 logits
-    rng = np.random.default_rng(wl.seed)
-    tok = np.sort(rng.choice(wl.T, size=min(64, wl.T), replace=False))
-    assert rel(logits[tok], O.router_logits(inp.x[tok], inp.wr)) <= TOL_BF16
-    # y, dx, dlogits of sampled tokens
-    fwd, bwd = sample_tokens(inp, logits, k, tok)
-    tsel = torch.from_numpy(tok).to(DEV)
-    errs = {"y": rel(host(layer.y[tsel]), fwd["y"]), "dx": rel(host(g.dx[tsel]), bwd["dx"]),
-            "dlogits": rel(host(layer.dlogits[tsel]), bwd["dz"]),
-            "dw_gate": rel(host(layer.dw[tsel]), bwd["dw"])}
-    # weight gradients of sampled experts: the hottest, the coldest non-empty, one random
-    nz = np.flatnonzero(counts)
-    experts = sorted({int(np.argmax(counts)), int(nz[np.argmin(counts[nz])]),
-                      int(rng.choice(nz))})
-    for e in experts:
-        rdw1, rdw2, n = expert_weight_grads(inp, k, oidx, ow, e)
-        gw1 = host(g.dw1[e])
-        errs[f"dw1_gate[{e}]"] = rel(gw1[:, :wl.F], rdw1[:, :wl.F])
-        errs[f"dw1_up[{e}]"] = rel(gw1[:, wl.F:], rdw1[:, wl.F:])
-        errs[f"dw2[{e}]"] = rel(host(g.dw2[e]), rdw2)
-    # router weight gradient: the product x^T @ dlogits of the device's dlogits
-    dl = host(layer.dlogits)
-    errs["dwr"] = rel(host(g.dwr), inp.x.astype(np.float64).T @ dl)
+    assert rel(host(layer.w), fwd["w"]) <= TOL_F32
+    errs["y"] = rel(host(layer.y), fwd["y"])
+    bwd = O.layer_backward(fwd, inp.dy, inp.x, inp.wr, inp.w1, inp.w2, k)
+    del fwd
+    say("  oracle backward done")
+    errs.update({"dx": rel(host(g.dx), bwd["dx"]), "dlogits": rel(host(layer.dlogits), bwd["dz"]),
+                 "dw_gate": rel(host(layer.dw), bwd["dw"]), "dwr": rel(host(g.dwr), bwd["dwr"]),
+                 "dw1_gate": rel_by_expert(g.dw1, bwd["dw1"], slice(0, wl.F)),
+                 "dw1_up": rel_by_expert(g.dw1, bwd["dw1"], slice(wl.F, 2 * wl.F)),
+                 "dw2": rel_by_expert(g.dw2, bwd["dw2"])})
     say("  errors", {k2: float("%.3g" % v) for k2, v in errs.items()})
-    assert max(errs.values()) <= TOL_BF16, errs
+    assert max(v for k2, v in errs.items() if k2 != "logits") <= TOL_BF16, errs
     # empty experts have exactly zero weight gradients
-    for e in np.flatnonzero(counts == 0)[:4]:
-        assert not host(g.dw2[int(e)]).any()
+    for e in np.flatnonzero(counts == 0):
+        assert not host(g.dw1[int(e)]).any() and not host(g.dw2[int(e)]).any()
 
 
 def test_layer_fused_activation_matches_unfused():

@@ -140,3 +140,57 @@ def test_count_index_skewed_and_empty():
     # All slots on one expert; most experts empty.
     _check_ci(np.full((5000, 1), 7, dtype=np.int32), 1024)
     _check_ci(np.full((3, 1), 0, dtype=np.int32), 1)
+
+
+# ------------------------------------------------------------------ non-finite logits
+@pytest.mark.parametrize("E,k", [(8, 2), (64, 8), (200, 8), (1024, 32)])
+def test_route_nan_and_inf_rows(E, k):
+    """Rows holding NaN or +-inf: the ids follow the oracle's stable
+    descending sort with NaNs last (NaNs in index order), so every token
+    still gets k distinct ids in [0, E), and counting gives a permutation."""
+    T = 64
+    say(f"route_topk non-finite rows E={E} k={k}")
+    logits = _logits(T, E, 41 + E, False)
+    g = np.random.default_rng(E)
+    logits[0, :] = np.nan                                   # all NaN
+    logits[1, g.choice(E, size=E // 2, replace=False)] = np.nan  # half NaN
+    logits[2, :] = -np.inf                                  # all -inf
+    logits[3, : E // 2] = np.nan
+    logits[3, E // 2:] = -np.inf                            # NaN below -inf
+    logits[4, g.choice(E, size=min(3, E), replace=False)] = np.inf
+    logits[5, :] = np.inf
+    idx, w, p = _run_route(logits, k)
+    oi, _, _ = O.route(logits, k)
+    np.testing.assert_array_equal(idx, oi)
+    assert ((idx >= 0) & (idx < E)).all()
+    for t in range(T):
+        assert len(set(idx[t].tolist())) == k
+    # finite rows keep finite weights
+    assert np.isfinite(w[6:]).all()
+    counts, offsets, dest, src = _run_count_index(idx.astype(np.int32), E)
+    assert sorted(dest.tolist()) == list(range(T * k))
+    np.testing.assert_array_equal(src[dest], np.arange(T * k))
+    np.testing.assert_array_equal(counts, O.count_tokens(oi, E))
+
+
+def test_out_of_range_ids_are_clamped():
+    """Expert ids outside [0, E) are caller errors; the kernels clamp them into
+    range (so the row maps stay a permutation and no index leaves its
+    buffer): forced ids in moe_route_topk, any id in moe_count_index."""
+    T, k, E = 300, 4, 16
+    say("out-of-range ids clamped")
+    ids = random_topk_ids(T, k, E, seed=9)
+    ids[0, 0] = -7
+    ids[5, 1] = E
+    ids[9, 3] = 10 * E
+    ids[17, 2] = -(1 << 30)
+    clamped = np.clip(ids, 0, E - 1).astype(np.int32)
+    got = _run_count_index(ids, E)
+    want = O.build_index(clamped, E)
+    for name, gv, wv in zip(("counts", "offsets", "dest", "src"), got, want):
+        np.testing.assert_array_equal(gv, wv, err_msg=name)
+    logits = _logits(T, E, 77, False)
+    idx, w, _ = _run_route(logits, k, forced=ids)
+    np.testing.assert_array_equal(idx, clamped)
+    _, ow, _ = O.route(logits, k, forced_idx=clamped)
+    assert rel(w, ow) <= TOL_F32
