@@ -139,6 +139,27 @@ moe_status moe_count_index(const int32_t* topk_idx, int T, int k, int E,
                            moe_stream_t stream);
 
 /*
+ * moe_count_index_noalloc -- moe_count_index for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and the same results,
+ * with the block tables in a static device array of MOE_NOALLOC_SCRATCH_BYTES
+ * per GPU (held from the first call on a device until the process ends)
+ * instead of a caller workspace.  It calls no allocating routine.
+ * Limit: moe_count_index_workspace_size(T, k, E) <= MOE_NOALLOC_SCRATCH_BYTES
+ * (e.g. T*k <= 1 Mi slots at E = 256, 256 Ki slots at E = 1024); larger
+ * shapes return MOE_ERR_UNSUPPORTED.  Every word of the array is written
+ * before it is read, so nothing is cleared between calls.  Every call on one
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and give undefined results; calls ordered on
+ * one stream are safe.  Other arguments and errors as moe_count_index.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (4u << 20)
+moe_status moe_count_index_noalloc(const int32_t* topk_idx, int T, int k, int E,
+                                   int32_t* counts, int32_t* offsets,
+                                   int32_t* dest, int32_t* src,
+                                   moe_stream_t stream);
+
+/*
  * moe_permute -- copy token rows into expert-contiguous order:
  * xp[dest[t*k + j], :] = x[t, :] for every slot (t, j), i.e.
  * xp[p, :] = x[src[p] / k, :].  The expert computation on the pages runs on

@@ -27,11 +27,13 @@ MOE_F32 = 0
 MOE_BF16 = 1
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 32
+MOE_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 # Every exported symbol of include/moe.h.
 SYMBOLS = (
     "moe_last_error", "moe_version", "moe_route_topk", "moe_route_topk_bwd",
-    "moe_count_index_workspace_size", "moe_count_index", "moe_permute",
+    "moe_count_index_workspace_size", "moe_count_index", "moe_count_index_noalloc",
+    "moe_permute",
     "moe_unpermute", "moe_unpermute_bwd", "moe_grouped_gemm_workspace_size",
     "moe_grouped_gemm_plan",
     "moe_grouped_gemm_fwd", "moe_grouped_gemm_bwd", "moe_grouped_gemm_swiglu_fwd",
@@ -89,6 +91,7 @@ _SIG = {
     "moe_route_topk_bwd": ([_p, _p, _p, _i, _i, _i, _i, _p, _i, _p], _i),
     "moe_count_index_workspace_size": ([_i, _i, _i], _z),
     "moe_count_index": ([_p, _i, _i, _i, _p, _p, _p, _p, _p, _z, _p], _i),
+    "moe_count_index_noalloc": ([_p, _i, _i, _i, _p, _p, _p, _p, _p], _i),
     "moe_permute": ([_p, _p, _i, _i, _i, _i, _p, _p], _i),
     "moe_unpermute": ([_p, _p, _p, _i, _i, _i, _i, _p, _p], _i),
     "moe_unpermute_bwd": ([_p, _p, _p, _p, _i, _i, _i, _i, _p, _p, _p], _i),
@@ -181,6 +184,11 @@ def moe_count_index(topk_idx, T, k, E, counts, offsets, dest, src, ws, ws_bytes,
     _check(_lib.moe_count_index(_ptr(topk_idx), T, k, E, _ptr(counts), _ptr(offsets),
                                 _ptr(dest), _ptr(src), _ptr(ws), ws_bytes,
                                 _stream(stream, topk_idx)))
+
+
+def moe_count_index_noalloc(topk_idx, T, k, E, counts, offsets, dest, src, stream=None):
+    _check(_lib.moe_count_index_noalloc(_ptr(topk_idx), T, k, E, _ptr(counts), _ptr(offsets),
+                                        _ptr(dest), _ptr(src), _stream(stream, topk_idx)))
 
 
 def moe_permute(x, dest, T, k, d, dtype, xp, stream=None):

@@ -21,6 +21,9 @@
 //               64-lane match mask (one ballot per expert-id bit), adds the
 //               running per-(wave, expert) count and the block offset, and
 //               writes dest and src.
+#include <mutex>
+#include <string>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -299,11 +302,11 @@ extern "C" size_t moe_count_index_workspace_size(int T, int k, int E) {
   return 2 * half;
 }
 
-extern "C" moe_status moe_count_index(const int32_t* topk_idx, int T, int k, int E,
-                                      int32_t* counts, int32_t* offsets, int32_t* dest,
-                                      int32_t* src, void* ws, size_t ws_bytes,
-                                      moe_stream_t stream) {
-  clear_error();
+namespace moe {
+namespace {
+
+moe_status check_count_index(const int32_t* topk_idx, int T, int k, int E, int32_t* counts,
+                             int32_t* offsets, int32_t* dest, int32_t* src) {
   MOE_REQUIRE(T >= 1 && k >= 1 && E >= 1, MOE_ERR_INVALID_ARG,
               "moe_count_index: T, k, E must be >= 1");
   MOE_REQUIRE(k <= E, MOE_ERR_INVALID_ARG, "moe_count_index: need k <= E");
@@ -312,11 +315,15 @@ extern "C" moe_status moe_count_index(const int32_t* topk_idx, int T, int k, int
   MOE_REQUIRE(Tk < (1ll << 31), MOE_ERR_UNSUPPORTED, "moe_count_index: T*k must be < 2^31");
   MOE_REQUIRE(topk_idx && counts && offsets && dest && src, MOE_ERR_INVALID_ARG,
               "moe_count_index: null pointer");
-  const size_t need = moe_count_index_workspace_size(T, k, E);
-  MOE_REQUIRE(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE,
-              "moe_count_index: workspace too small");
-  MOE_REQUIRE((reinterpret_cast<uintptr_t>(ws) & 15) == 0, MOE_ERR_WORKSPACE,
-              "moe_count_index: workspace must be 16-byte aligned");
+  return MOE_OK;
+}
+
+// The launches of moe_count_index over a validated workspace of `need` bytes
+// (every word of it is written before it is read: no clearing needed).
+moe_status count_index_launch(const int32_t* topk_idx, int T, int k, int E, int32_t* counts,
+                              int32_t* offsets, int32_t* dest, int32_t* src, void* ws,
+                              size_t need, moe_stream_t stream) {
+  const long long Tk = static_cast<long long>(T) * k;
   const int nblk = num_chunks(Tk);
   int32_t* blk_cnt = static_cast<int32_t*>(ws);
   int32_t* blk_off = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + need / 2);
@@ -337,4 +344,68 @@ extern "C" moe_status moe_count_index(const int32_t* topk_idx, int T, int k, int
                      kCiWaves * E * sizeof(int32_t), st, topk_idx, static_cast<int>(Tk), E,
                      id_bits(E), nblk, blk_off, dest, src);
   return check_launch("moe_count_index/scatter");
+}
+
+// Scratch of moe_count_index_noalloc: one copy per GPU, held until the
+// process ends.  Host code never names this array in a device context (on
+// the host its name is only a stand-in); it uses the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+moe_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  MOE_REQUIRE(err == hipSuccess, MOE_ERR_HIP,
+              std::string("moe_count_index_noalloc: hipGetDevice: ") + hipGetErrorString(err));
+  MOE_REQUIRE(dev >= 0 && dev < kMaxDevices, MOE_ERR_UNSUPPORTED,
+              "moe_count_index_noalloc: device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    MOE_REQUIRE(err == hipSuccess && p != nullptr, MOE_ERR_HIP,
+                std::string("moe_count_index_noalloc: hipGetSymbolAddress: ") +
+                    hipGetErrorString(err));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status moe_count_index(const int32_t* topk_idx, int T, int k, int E,
+                                      int32_t* counts, int32_t* offsets, int32_t* dest,
+                                      int32_t* src, void* ws, size_t ws_bytes,
+                                      moe_stream_t stream) {
+  clear_error();
+  if (moe_status s = check_count_index(topk_idx, T, k, E, counts, offsets, dest, src)) return s;
+  const size_t need = moe_count_index_workspace_size(T, k, E);
+  MOE_REQUIRE(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE,
+              "moe_count_index: workspace too small");
+  MOE_REQUIRE((reinterpret_cast<uintptr_t>(ws) & 15) == 0, MOE_ERR_WORKSPACE,
+              "moe_count_index: workspace must be 16-byte aligned");
+  return count_index_launch(topk_idx, T, k, E, counts, offsets, dest, src, ws, need, stream);
+}
+
+extern "C" moe_status moe_count_index_noalloc(const int32_t* topk_idx, int T, int k, int E,
+                                              int32_t* counts, int32_t* offsets, int32_t* dest,
+                                              int32_t* src, moe_stream_t stream) {
+  clear_error();
+  if (moe_status s = check_count_index(topk_idx, T, k, E, counts, offsets, dest, src)) return s;
+  const size_t need = moe_count_index_workspace_size(T, k, E);
+  MOE_REQUIRE(need <= MOE_NOALLOC_SCRATCH_BYTES, MOE_ERR_UNSUPPORTED,
+              "moe_count_index_noalloc: the block tables of this shape exceed the static "
+              "scratch (moe_count_index_workspace_size(T, k, E) must be <= "
+              "MOE_NOALLOC_SCRATCH_BYTES); use moe_count_index with a workspace");
+  void* ws = nullptr;
+  if (moe_status s = scratch_of_current_device(&ws)) return s;
+  return count_index_launch(topk_idx, T, k, E, counts, offsets, dest, src, ws, need, stream);
 }

@@ -132,6 +132,20 @@ def test_gathered_gemm_validation():
     assert bw(a14=FAKE + 4) == L.MOE_ERR_INVALID_ARG     # misaligned db
 
 
+def test_count_index_noalloc_validation():
+    """The allocation-free variant validates like moe_count_index and refuses
+    shapes whose block tables exceed its static scratch, all before any
+    device call."""
+    assert L.MOE_NOALLOC_SCRATCH_BYTES == 4 << 20
+    assert _rc("moe_count_index_noalloc", FAKE, 0, 2, 4, FAKE, FAKE, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert _rc("moe_count_index_noalloc", FAKE, 16, 5, 4, FAKE, FAKE, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert _rc("moe_count_index_noalloc", None, 16, 2, 4, FAKE, FAKE, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    T, k, E = 262656, 1, 1024
+    assert L.moe_count_index_workspace_size(T, k, E) > L.MOE_NOALLOC_SCRATCH_BYTES
+    assert _rc("moe_count_index_noalloc", FAKE, T, k, E, FAKE, FAKE, FAKE, FAKE, None) == L.MOE_ERR_UNSUPPORTED
+    assert "scratch" in L.moe_last_error()
+
+
 def test_layer_refuses_mismatched_inputs():
     """MoELayer checks every input against its shape, dtype and device before
     any library call (the kernels size buffer ranges from the layer's shape,
