@@ -67,6 +67,7 @@ def call_work(wl, b):
     f["permute"] = (0, T * d * b + Tk * d * b + Tk * 4)
     f["gemm1_fwd"] = (2 * Tk * d * 2 * F, Tk * d * b + E * d * 2 * F * b + Tk * 2 * F * b)
     f["act_fwd"] = (0, Tk * 2 * F * b + Tk * F * b)
+    f["act_fwd_recompute"] = f["act_fwd"]  # the same kernel, in the backward pass
     f["gemm1_swiglu_fwd"] = (f["gemm1_fwd"][0], f["gemm1_fwd"][1] + Tk * F * b)
     f["gemm2_fwd"] = (2 * Tk * F * d, Tk * F * b + E * F * d * b + Tk * d * b)
     f["unpermute"] = (0, Tk * d * b + T * d * b + Tk * 8)
@@ -316,6 +317,13 @@ def summarize_busy(directory, trace_dir, out, command, command_trace, workload):
     counters = ("GRBM_GUI_ACTIVE", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES",
                 "SQ_INSTS_VALU_MFMA_MOPS_BF16")
     vals = {c: _per_kernel(directory, c) for c in counters}
+    # Each dispatch's own duration in the (serialised) counter pass, for the
+    # clock: GRBM_GUI_ACTIVE counts the cycles of that same interval.
+    pmc_ns = {}
+    for r in _csv_rows(directory, "_counter_collection.csv"):
+        if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+            pmc_ns.setdefault(r["Kernel_Name"], []).append(
+                float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
     durs = {}
     for r in _csv_rows(trace_dir, "_kernel_stats.csv"):
         durs[_short(r["Name"])] = float(r["AverageNs"])
@@ -325,13 +333,21 @@ def summarize_busy(directory, trace_dir, out, command, command_trace, workload):
     lines = [f"# Clock and MFMA activity of the grouped-GEMM kernels, workload {workload}", "",
              f"command (--pmc pass): {command}",
              f"command (--kernel-trace --stats pass): {command_trace}", "",
-             "Per dispatch (mean over dispatches).  clock = GRBM_GUI_ACTIVE / average "
-             "duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 256 CUs x 4 "
-             "SIMDs); executed / algorithmic = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / "
-             "algorithmic FLOPs.", "",
-             "| kernel | calls | avg us | GRBM_GUI_ACTIVE | clock GHz | SQ_BUSY_CYCLES | "
-             "MFMA busy cycles | MFMA busy / (active x 1024) | executed / algorithmic |",
-             "|---|---|---|---|---|---|---|---|---|"]
+             "Per dispatch (mean over dispatches).  GRBM_GUI_ACTIVE is summed over the 8 XCDs "
+             "(the agent reports Num_Xcc 8, 1024 SIMDs, max engine clock 2400 MHz): busy "
+             "cycles per XCD = GRBM_GUI_ACTIVE / 8, effective clock = that / the dispatch's "
+             "own duration in the counter pass (its start and end timestamps; dispatches are "
+             "serialised there).  SQ_VALU_MFMA_BUSY_CYCLES is summed over the SIMDs, so MFMA "
+             "busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs) is the "
+             "fraction of the chip's MFMA issue slots at the clock it ran at, and clock / "
+             "2.4 GHz x MFMA busy is the fraction of the 2.5 PFLOP/s peak.  'trace avg us' is "
+             "the kernel's average duration in the --kernel-trace --stats pass (kernels of "
+             "one call per row only when the kernel serves one call).  executed / "
+             "algorithmic = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / algorithmic FLOPs.", "",
+             "| kernel (calls) | dispatches | trace avg us | counter-pass us | "
+             "GRBM_GUI_ACTIVE / 8 | clock GHz | SQ_BUSY_CYCLES | MFMA busy cycles | MFMA busy | "
+             "clock/2.4 x busy | executed / algorithmic |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
     for name in sorted(vals["GRBM_GUI_ACTIVE"]):
         if "gemm_mfma_kernel" not in name:
             continue
@@ -341,14 +357,16 @@ def summarize_busy(directory, trace_dir, out, command, command_trace, workload):
         dur = durs.get(short)
         calls = names.get(short, [])
         alg = sum(work[c][0] for c in calls) / len(calls) if calls else 0
-        act = mean["GRBM_GUI_ACTIVE"]
-        clock = act / dur if dur else float("nan")
+        act = mean["GRBM_GUI_ACTIVE"] / 8
+        pns = pmc_ns.get(name, [])
+        pdur = sum(pns) / len(pns) if pns else 0.0
+        clock = act / pdur if pdur else float("nan")
         busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (act * 1024) if act else float("nan")
         ratio = mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / alg if alg else float("nan")
         lines.append(f"| {short} ({', '.join(calls)}) | {len(vals['GRBM_GUI_ACTIVE'][name])} | "
-                     f"{(dur or 0) / 1e3:.1f} | {act:.0f} | {clock:.3f} | "
+                     f"{(dur or 0) / 1e3:.1f} | {pdur / 1e3:.1f} | {act:.0f} | {clock:.3f} | "
                      f"{mean['SQ_BUSY_CYCLES']:.0f} | {mean['SQ_VALU_MFMA_BUSY_CYCLES']:.0f} | "
-                     f"{busy:.3f} | {ratio:.3f} |")
+                     f"{busy:.3f} | {clock / 2.4 * busy:.3f} | {ratio:.3f} |")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -569,7 +587,7 @@ def measure(wl, args, detail):
         rec["note"] = ("float32 layer: FMA kernels (no bf16 MFMA path); the bf16 fractions "
                        "do not apply")
 
-    if detail and not args.overlap_wgrad and not args.graph:
+    if detail and not args.overlap_wgrad and not args.graph and not args.no_overlap_variant:
         # The same step with the expert weight-gradient GEMMs on a second
         # stream (beside the data-gradient chain), timed after everything
         # above so that the per-kernel figures stay those of one stream.
@@ -592,6 +610,35 @@ def measure(wl, args, detail):
             "note": "weight-gradient GEMMs on a second stream; not the headline: "
                     "overlapped kernels stretch each other's measured durations"}
         del lay2
+
+    if (detail or wl.name == "olmoe") and not args.no_overlap_variant:
+        # Selective recomputation (activation checkpointing of the layer):
+        # what each mode keeps between the passes, and its step time.
+        lay3 = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, dtype=tdt, device=dev)
+        rc = {}
+        for mode in MoELayer.RECOMPUTE:
+            lay3.recompute = mode
+
+            def step3():
+                lay3.forward(x, wr, w1, w2, bias=bias, forced_idx=forced)
+                lay3.backward(dy)
+
+            for _ in range(max(1, args.warmup)):
+                step3()
+            torch.cuda.synchronize()
+            r0 = time.perf_counter()
+            for _ in range(args.steps):
+                step3()
+            torch.cuda.synchronize()
+            r_ms = (time.perf_counter() - r0) * 1e3 / args.steps
+            rc[mode] = {"ms_per_step": round(r_ms, 4),
+                        "saved_bytes": int(sum(lay3.saved_bytes(mode).values()))}
+        for mode in ("act", "layer"):
+            rc[mode]["time_cost_pct"] = round(
+                100 * (rc[mode]["ms_per_step"] / rc["none"]["ms_per_step"] - 1), 2)
+            rc[mode]["memory_saved_bytes"] = rc["none"]["saved_bytes"] - rc[mode]["saved_bytes"]
+        rec["recompute"] = rc
+        del lay3
 
     if detail and args.copy_probe:
         n = 1 << 30
@@ -650,6 +697,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time replays of the step captured as a HIP graph (headline "
                          "workload; per-kernel figures still come from eager steps)")
+    ap.add_argument("--no-overlap-variant", action="store_true",
+                    help="skip the two-stream variant of the headline workload (profiling "
+                         "runs: overlapped kernels stretch each other's durations)")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="write a text summary of a rocprofv3 --kernel-trace --stats output")

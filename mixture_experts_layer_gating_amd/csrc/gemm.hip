@@ -70,6 +70,7 @@ struct GemmArgs {
   unsigned xmagic;  // ceil(2^32 / xdiv) mod 2^32 (see div_rows)
   int xshift;       // log2(xdiv) when xdiv is a power of two, else -1
   int hot_first;    // TN, E <= 256: take the groups in hot-first order (group_at)
+  int row_group;    // NN / NT: tile order inside a group (see find_row_tile); 0 = row-major
 };
 
 // ------------------------------------------------------------------ tiles
@@ -77,16 +78,40 @@ struct GemmArgs {
 // workgroup's row tile (the same answer in each wave, so no LDS and no
 // barrier are needed, and small tiles keep their LDS footprint at a multiple
 // of the operand buffers).  Tiles are counted per expert as
-// ceil(rows_e / BM); logical tile L = row_tile * ntn + col_tile; workgroup b
-// runs on XCD b % 8 and takes logical tile (b % 8) * ceil(n / 8) + b / 8.  Up
-// to kHeld * 64 experts the offsets are loaded once (all loads in flight
-// together) and kept in registers.
+// ceil(rows_e / BM); expert e owns logical tiles [ntn * first_row_tile_e,
+// ntn * (first_row_tile_e + tiles_e)), ordered inside by order_in_group;
+// workgroup b runs on XCD b % 8 and takes logical tile
+// (b % 8) * ceil(n / 8) + b / 8, so each XCD walks a contiguous range of
+// experts.  Up to kHeld * 64 experts the offsets are loaded once (all loads in
+// flight together) and kept in registers.
 struct RowTile {
   int found, e, mt_local, nt, g0, g1;  // wave-uniform
 };
 
+// Position of the tile at index `local` among a group's te * ntn tiles.
+// group_rows = 0: row-major (all ntn column tiles of a row tile in turn).
+// Otherwise the group's row tiles are taken in bands of group_rows, and each
+// band column by column: the ~32 tiles an XCD runs at once then cover a few
+// row tiles and a few column tiles of one group (e.g. 8 x 4) instead of two
+// row tiles and every column tile, so fewer distinct operand slabs stream
+// through that XCD's L2 at a time.
+__device__ __forceinline__ void order_in_group(int local, int te, int ntn, int group_rows,
+                                               int& mt_local, int& nt) {
+  if (group_rows <= 0) {
+    mt_local = local / ntn;
+    nt = local - mt_local * ntn;
+    return;
+  }
+  const int band = local / (group_rows * ntn);
+  const int rows = min(group_rows, te - band * group_rows);
+  const int w = local - band * group_rows * ntn;
+  nt = w / rows;
+  mt_local = band * group_rows + (w - nt * rows);
+}
+
 template <int BM>
-__device__ RowTile find_row_tile(const int32_t* __restrict__ offsets, int E, int ntn, int lane) {
+__device__ RowTile find_row_tile(const int32_t* __restrict__ offsets, int E, int ntn,
+                                 int group_rows, int lane) {
   constexpr int kHeld = 4;
   const bool held = E <= kHeld * kWave;
   int o0[kHeld], o1[kHeld], tiles[kHeld], incl[kHeld];
@@ -121,8 +146,11 @@ __device__ RowTile find_row_tile(const int32_t* __restrict__ offsets, int E, int
   const long long L = static_cast<long long>(blockIdx.x & 7) * per + rank;
   int found = 0, e_found = 0, mt_local = 0, nt = 0, g0 = 0, g1 = 0;
   if (rank < per && L < n_act) {
+    // Group e owns logical tiles [ntn * excl_e, ntn * (excl_e + tiles_e)), so
+    // the row tile L / ntn (counted over all groups) names the group; the
+    // tile's place inside the group follows order_in_group.
     const int mt = static_cast<int>(L / ntn);
-    nt = static_cast<int>(L - static_cast<long long>(mt) * ntn);
+    int excl_found = 0, te_found = 0;
     int carry = 0;
     if (held) {
 #pragma unroll
@@ -134,7 +162,8 @@ __device__ RowTile find_row_tile(const int32_t* __restrict__ offsets, int E, int
         if (bal) {
           const int srcl = __builtin_ctzll(bal);
           e_found = c * kWave + srcl;
-          mt_local = mt - __shfl(excl, srcl, kWave);
+          excl_found = __shfl(excl, srcl, kWave);
+          te_found = __shfl(tiles[c], srcl, kWave);
           g0 = __shfl(o0[c], srcl, kWave);
           g1 = __shfl(o1[c], srcl, kWave);
           found = 1;
@@ -154,7 +183,8 @@ __device__ RowTile find_row_tile(const int32_t* __restrict__ offsets, int E, int
         if (bal) {
           const int srcl = __builtin_ctzll(bal);
           e_found = __shfl(e, srcl, kWave);
-          mt_local = mt - __shfl(excl, srcl, kWave);
+          excl_found = __shfl(excl, srcl, kWave);
+          te_found = __shfl(n, srcl, kWave);
           g0 = __shfl(a0, srcl, kWave);
           g1 = __shfl(a1, srcl, kWave);
           found = 1;
@@ -162,6 +192,10 @@ __device__ RowTile find_row_tile(const int32_t* __restrict__ offsets, int E, int
         }
         carry += __shfl(inc, kWave - 1, kWave);
       }
+    }
+    if (found) {
+      const int local = static_cast<int>(L - static_cast<long long>(excl_found) * ntn);
+      order_in_group(local, te_found, ntn, group_rows, mt_local, nt);
     }
   }
   return RowTile{found, e_found, mt_local, nt, g0, g1};
@@ -255,7 +289,7 @@ __device__ bool resolve_tile(const GemmArgs& p, TileInfo& t) {
     return true;
   } else {
     const int lane = threadIdx.x & (kWave - 1);
-    const RowTile r = find_row_tile<BM>(p.offsets, p.E, p.ntn, lane);
+    const RowTile r = find_row_tile<BM>(p.offsets, p.E, p.ntn, p.row_group, lane);
     if (!r.found) return false;
     t.e = r.e;
     t.g0 = r.g0;
@@ -1115,6 +1149,13 @@ struct Cfg {
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
+// Row tiles per band of the row-tiled tile order (order_in_group).  Measured
+// (interleaved runs, whole layer): large-expert step 16.05 ms with row-major
+// order, 15.68 ms with bands of 4, 15.60 ms with bands of 8 (GEMM 1's data
+// gradient -8%, GEMM 2 forward -6%); OLMoE-like 3.015 / 3.016 / 2.98 ms.
+constexpr int kRowGroup = 8;
+int row_group_rows() { return kRowGroup; }
+
 // Tile shape for the row-tiled modes from the mean rows per expert and the
 // number of output columns.
 Cfg pick_row_cfg(int M, int E, int ncols) {
@@ -1181,6 +1222,7 @@ template <int MODE, typename OutT, bool GX = false>
 void dispatch_mfma(Cfg c, GemmArgs p, hipStream_t st) {
   const int ncols = (MODE == kNN) ? p.N : (MODE == kNT ? p.K : p.N);
   p.ntn = static_cast<int>(ceil_div(ncols, c.bn));
+  p.row_group = row_group_rows();
   long long upper;
   if (MODE == kTN) {
     // 8 XCDs x (tile rows per XCD, whole deals) x ntn
@@ -1206,6 +1248,7 @@ Cfg pick_glu_cfg(int M, int E, int N) {
 template <bool GX = false>
 void dispatch_glu(Cfg c, GemmArgs p, hipStream_t st) {
   p.ntn = static_cast<int>(ceil_div(p.N / 2, c.bn / 2));
+  p.row_group = row_group_rows();
   const long long upper = (ceil_div(p.M, c.bm) + p.E) * p.ntn;
   if (c.bm == 256 && c.bn == 256)
     launch_mfma<kNN, 256, 256, 2, 4, uint16_t, true, GX>(p, upper, st);

@@ -55,12 +55,26 @@ class MoELayer:
     the same bits either way.  Inputs are passed to :meth:`forward`; the returned
     tensors are views of buffers owned by the layer and are overwritten by the
     next call.
+
+    ``recompute`` selects what the backward pass recomputes instead of reading
+    it from the forward pass (selective activation checkpointing of the MoE
+    layer [Brief, Core method: SAC over norm, attention and the sparse MoE]):
+    ``"none"`` keeps every intermediate; ``"act"`` does not keep the SwiGLU
+    output ``a`` (the backward recomputes it from ``h`` before GEMM 2's weight
+    gradient); ``"layer"`` keeps only the layer's inputs (the backward re-runs
+    the whole forward first).  Results are the same bits in every mode;
+    :meth:`saved_bytes` gives what each mode keeps between the passes.
     """
 
+    RECOMPUTE = ("none", "act", "layer")
+
     def __init__(self, T, d, E, k, F, dtype=torch.bfloat16, device="cuda", renorm=False,
-                 fuse_act=True, overlap_wgrad=False, gather_x=True):
+                 fuse_act=True, overlap_wgrad=False, gather_x=True, recompute="none"):
         if not (1 <= k <= E):
             raise ValueError("need 1 <= k <= E")
+        if recompute not in self.RECOMPUTE:
+            raise ValueError(f"recompute must be one of {self.RECOMPUTE}")
+        self.recompute = recompute
         self.T, self.d, self.E, self.k, self.F = T, d, E, k, F
         self.dtype = dtype
         self.code = L.dtype_code(dtype)
@@ -188,8 +202,25 @@ class MoELayer:
                                    stream=s)
         with self._span("unpermute"):
             L.moe_unpermute(self.yp, self.dest, self.w, T, k, d, c, self.y, stream=s)
-        self._inputs = (x, wr, w1, w2)
+        self._inputs = (x, wr, w1, w2, bias, forced_idx)
         return self.y
+
+    def saved_bytes(self, recompute=None):
+        """Bytes of the forward-pass results the backward pass reads (what an
+        activation-memory budget must hold between the two passes), by
+        tensor, for ``recompute`` (default: the layer's own mode).  The
+        layer's inputs (x, weights, bias, forced ids) are not counted: the
+        caller keeps them in every mode."""
+        mode = self.recompute if recompute is None else recompute
+        if mode not in self.RECOMPUTE:
+            raise ValueError(f"recompute must be one of {self.RECOMPUTE}")
+        if mode == "layer":
+            return {}
+        kept = {n: getattr(self, n) for n in ("probs", "idx", "w", "offsets", "dest", "src",
+                                               "h", "a", "yp")}
+        if mode == "act":
+            del kept["a"]
+        return {n: t.numel() * t.element_size() for n, t in kept.items()}
 
     def capture(self, x, wr, w1, w2, dy, bias=None, forced_idx=None):
         """Record one forward + backward over these input buffers as a HIP
@@ -234,22 +265,33 @@ class MoELayer:
     def backward(self, dy, stream=None):
         if self._inputs is None:
             raise RuntimeError("backward() before forward()")
-        x, wr, w1, w2 = self._inputs
+        x, wr, w1, w2, bias, forced_idx = self._inputs
         T, d, E, k, F, Tk, c = self.T, self.d, self.E, self.k, self.F, self.Tk, self.code
         if dy is None:
             raise ValueError("dy is required")
         self._expect(dy, "dy", (T, d), self.dtype)
         s = stream
+        if self.recompute == "layer":
+            # Only the inputs were kept: recompute every forward result first
+            # (logits, routing, indices, h, a, yp; y is rewritten unchanged).
+            self.forward(x, wr, w1, w2, bias=bias, forced_idx=forced_idx, stream=s)
         ws, wsb = self.gemm_ws, self.gemm_ws_bytes
         overlap = self.overlap_wgrad and (s is None or isinstance(s, torch.cuda.Stream))
         main = (s if s is not None else torch.cuda.current_stream(self.device)) if overlap else s
         with self._span("unpermute_bwd"):
             L.moe_unpermute_bwd(dy, self.yp, self.dest, self.w, T, k, d, c, self.dyp, self.dw,
                                 stream=main)
+        if self.recompute == "act":
+            # a was not kept: recompute it from the stored h (the same
+            # arithmetic as GEMM 1's activation epilogue, so the same bits)
+            # for GEMM 2's weight gradient.
+            with self._span("act_fwd_recompute"):
+                L.moe_act_fwd(self.h, Tk, F, c, self.a, stream=main)
         if overlap:
             self.ev_dyp.record(main)
         with self._span("gemm2_bwd_da"):
-            L.moe_grouped_gemm_bwd(self.a, w2, self.dyp, self.offsets, Tk, F, d, E, c, self.da,
+            # data gradient only: the activation operand `a` is not read
+            L.moe_grouped_gemm_bwd(None, w2, self.dyp, self.offsets, Tk, F, d, E, c, self.da,
                                    None, None, ws, wsb, stream=main)
         with self._span("act_bwd"):
             L.moe_act_bwd(self.h, self.da, Tk, F, c, self.dh, stream=main)

@@ -175,5 +175,15 @@ def test_layer_refuses_mismatched_inputs():
         with pytest.raises(ValueError):
             lay.forward(**args)
     assert lay.xp is None  # the gathered path keeps no permuted copy of x
+    # what each recompute mode keeps between the passes
+    Tk = T * k
+    full = lay.saved_bytes("none")
+    assert full["h"] == Tk * 2 * F * 2 and full["a"] == Tk * F * 2 and full["yp"] == Tk * d * 2
+    assert full["dest"] == full["src"] == Tk * 4 and full["probs"] == T * E * 4
+    act = lay.saved_bytes("act")
+    assert set(full) - set(act) == {"a"} and sum(full.values()) - sum(act.values()) == Tk * F * 2
+    assert lay.saved_bytes("layer") == {}
+    with pytest.raises(ValueError):
+        MoELayer(T, d, E, k, F, dtype=bf, device="cpu", recompute="all")
     with pytest.raises(RuntimeError):
         lay.backward(torch.zeros(T, d, dtype=bf))

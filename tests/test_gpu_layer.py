@@ -246,6 +246,45 @@ def test_layer_fused_activation_matches_unfused():
         np.testing.assert_array_equal(v, host(getattr(gb, k)), err_msg=k)
 
 
+@pytest.mark.parametrize("mode", ["act", "layer"])
+def test_layer_recompute_modes_match(mode):
+    """Selective recomputation: with recompute="act" the backward pass
+    recomputes the SwiGLU output from h, with "layer" it re-runs the whole
+    forward from the inputs.  Everything the mode does not keep is overwritten
+    with garbage between the passes, and the gradients must still be the bits
+    of the keep-everything layer."""
+    from mixture_experts_layer_gating_amd.layer import MoELayer
+    wl = Workload("recompute", T=1024, d=512, E=16, k=4, F=256, dtype="bf16", w_std=0.05,
+                  seed=43, regime="skew")
+    say(f"layer recompute={mode} {wl}")
+    inp = make_inputs(wl)
+    la, ga, args = _run(inp)
+    want = {n: host(getattr(ga, n)).copy() for n in ("dx", "dwr", "dw1", "dw2")}
+    want["y"] = host(la.y).copy()
+    x, wr, w1, w2, dy, bias, forced = args
+    lb = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, dtype=torch.bfloat16, device=DEV,
+                  recompute=mode)
+    for _ in range(2):
+        lb.forward(x, wr, w1, w2, bias=bias, forced_idx=forced)
+        lost = ["a"] if mode == "act" else ["logits", "probs", "idx", "w", "counts", "offsets",
+                                            "dest", "src", "h", "a", "yp", "y"]
+        for n in lost:
+            t = getattr(lb, n)
+            if t.dtype == torch.int32:
+                t.fill_(7)   # a valid but wrong row/expert everywhere
+            else:
+                t.fill_(float("nan"))
+        gb = lb.backward(dy)
+        torch.cuda.synchronize()
+        for n in ("dx", "dwr", "dw1", "dw2"):
+            np.testing.assert_array_equal(host(getattr(gb, n)), want[n], err_msg=n)
+        if mode == "layer":
+            np.testing.assert_array_equal(host(lb.y), want["y"])
+    kept = lb.saved_bytes()
+    full = lb.saved_bytes("none")
+    assert (kept == {}) if mode == "layer" else (set(full) - set(kept) == {"a"})
+
+
 def test_layer_overlapped_weight_gradients_match():
     """The weight-gradient GEMMs on a second stream give the same bits as the
     one-stream sequence, over two steps in a row (the second step's forward
