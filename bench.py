@@ -349,14 +349,17 @@ def summarize_busy(directory, trace_dir, out, command, command_trace, workload):
              "clock/2.4 x busy | executed / algorithmic |",
              "|---|---|---|---|---|---|---|---|---|---|---|"]
     for name in sorted(vals["GRBM_GUI_ACTIVE"]):
-        if "gemm_mfma_kernel" not in name:
+        lib = name.startswith("Cijk")  # the library GEMM of the reference product
+        if "gemm_mfma_kernel" not in name and not lib:
             continue
-        short = _short(name)
+        short = "hipBLASLt bf16 8192^3 (torch.matmul)" if lib else _short(name)
         mean = {c: (sum(vals[c].get(name, [0])) / max(1, len(vals[c].get(name, [0]))))
                 for c in counters}
-        dur = durs.get(short)
+        dur = durs.get(_short(name))
         calls = names.get(short, [])
         alg = sum(work[c][0] for c in calls) / len(calls) if calls else 0
+        if lib:
+            calls, alg = ["library reference"], 2.0 * 8192 ** 3
         act = mean["GRBM_GUI_ACTIVE"] / 8
         pns = pmc_ns.get(name, [])
         pdur = sum(pns) / len(pns) if pns else 0.0
