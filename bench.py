@@ -785,6 +785,7 @@ def main():
         "step_median": head["step_median"],
         "data_movement_frac_of_hbm": head["data_movement_frac_of_hbm"],
         "overlap_wgrad": head.get("overlap_wgrad"),
+        "recompute": head.get("recompute"),
         "library_gemm_reference": ref_gemm,
         "kernels": head["kernels"],
         "kernels_note": "per-call times from a pass of steps after the timed region",
