@@ -1202,8 +1202,12 @@ Waves waves_of(Cfg c) {
 // bytes.  Larger shapes take the FMA kernel.
 bool mfma_ok(moe_dtype dt, int M, int K, int N) {
   const long long lim = 1ll << 30;  // elements of 2 bytes
-  return dt == MOE_BF16 && K % 8 == 0 && N % 8 == 0 && static_cast<long long>(M) * K < lim &&
-         static_cast<long long>(M) * N < lim && static_cast<long long>(K) * N < lim;
+  // Tile-relative store offsets (up to 256 rows of a float32 row of K or N
+  // elements, added to the out-of-range base 2^31) must stay below 2^32.
+  const int row_lim = 1 << 20;
+  return dt == MOE_BF16 && K % 8 == 0 && N % 8 == 0 && K < row_lim && N < row_lim &&
+         static_cast<long long>(M) * K < lim && static_cast<long long>(M) * N < lim &&
+         static_cast<long long>(K) * N < lim;
 }
 
 // The MFMA kernels move 16-byte vectors: operands and results start on
