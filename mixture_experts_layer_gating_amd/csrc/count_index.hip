@@ -9,7 +9,7 @@
 // makes the result unique and deterministic.  No global atomics are used;
 // ranks come from wavefront ballots and LDS-staged scans.
 //
-// Three launches (two when the histogram table is small, see
+// Three launches (two when the histogram table's reads stay small, see
 // ci_scan_scatter_kernel: each scatter block then does its own scan):
 //   1. count:   block b histograms its chunk of slots in LDS
 //               -> blk_cnt[e][b]                                  (workspace)
@@ -210,14 +210,26 @@ __global__ __launch_bounds__(kCiBlock) void ci_scatter_kernel(
                 dest, src);
 }
 
-// Scan and scatter in one launch, for small histogram tables (E <= 256 and
-// E * nblk <= kFusedTable): every block sums the block histograms itself --
-// all blocks before it, and all blocks for the totals -- so no separate
-// single-block scan is launched.  Block 0 also writes counts and offsets.
-// Same arithmetic as ci_scan_kernel (integer sums), so the same result.
-constexpr int kFusedExperts = 256;
-constexpr int kFusedTable = 16384;  // ints of blk_cnt read by every block
+// Scan and scatter in one launch, for histogram tables whose reads stay small
+// (E <= 1024 and E * nblk^2 <= kFusedReads; every workload here): every block
+// sums the block histograms itself -- all blocks before it, and all blocks
+// for the totals -- so no separate single-block scan is launched.  Block 0
+// also writes counts and offsets.  Same arithmetic as ci_scan_kernel
+// (integer sums), so the same result.  (The separate single-block scan took
+// 56 us at the large-expert shape, E = 128 x 256 blocks; its lanes read runs
+// of counts 128 bytes apart, one cache line each.)
+constexpr int kFusedExperts = 1024;
+// Every block reads the whole E x nblk table, so the fused path reads
+// E * nblk^2 ints from L2 in all; above this the separate scan is cheaper.
+constexpr long long kFusedReads = 1ll << 24;
+// Tables up to this many ints are summed thread-per-expert (WAVE_ROWS =
+// false): many experts with few blocks each (sparse small groups: 14 us in
+// all against 35 us wave-per-expert, OLMoE-like 16.6 against 19.1 us);
+// larger ones wave-per-expert (large-expert shape: 36 us against 69 us with
+// the separate scan).
+constexpr int kThreadRowsTable = 16384;
 
+template <bool WAVE_ROWS>
 __global__ __launch_bounds__(kCiBlock) void ci_scan_scatter_kernel(
     const int32_t* __restrict__ ids, int Tk, int E, int nbits, int nblk,
     const int32_t* __restrict__ blk_cnt, int32_t* __restrict__ counts,
@@ -226,38 +238,75 @@ __global__ __launch_bounds__(kCiBlock) void ci_scan_scatter_kernel(
   __shared__ int32_t base_s[kFusedExperts];
   __shared__ int32_t run[kCiWaves * kFusedExperts];
   const int lane = threadIdx.x & (kWave - 1);
-  // tpe threads per expert, a power of two <= 64 with E * tpe <= kCiBlock,
-  // so an expert's threads share a wave.
-  int tpe = 1;
-  while (tpe < kWave && 2 * tpe * E <= kCiBlock) tpe *= 2;
-  const int per_t = (nblk + tpe - 1) / tpe;
-  const int e = threadIdx.x / tpe, sub = threadIdx.x % tpe;
-  const bool act = e < E;
-  const int b0 = min(nblk, sub * per_t), b1 = min(nblk, b0 + per_t);
-  const int32_t* row = blk_cnt + static_cast<size_t>(act ? e : 0) * nblk;
+  const int wid = threadIdx.x / kWave;
   const int me = static_cast<int>(blockIdx.x);
-  int before = 0, total = 0;
-  if (act) {
-    constexpr int kBatch = 8;  // loads in flight together
-    for (int b = b0; b < b1; b += kBatch) {
-      int v[kBatch];
+  if (!WAVE_ROWS) {
+    // Small tables: tpe threads per expert, a power of two <= 64 with
+    // E * tpe <= kCiBlock (an expert's threads share a wave), each summing a
+    // run of blocks, eight loads in flight at a time.
+    int tpe = 1;
+    while (tpe < kWave && 2 * tpe * E <= kCiBlock) tpe *= 2;
+    const int per_t = (nblk + tpe - 1) / tpe;
+    const int e = threadIdx.x / tpe, sub = threadIdx.x % tpe;
+    const bool act = e < E;
+    const int b0 = min(nblk, sub * per_t), b1 = min(nblk, b0 + per_t);
+    const int32_t* row = blk_cnt + static_cast<size_t>(act ? e : 0) * nblk;
+    int before = 0, total = 0;
+    if (act) {
+      constexpr int kBatch = 8;
+      for (int b = b0; b < b1; b += kBatch) {
+        int v[kBatch];
 #pragma unroll
-      for (int q = 0; q < kBatch; ++q) v[q] = b + q < b1 ? row[b + q] : 0;
+        for (int q = 0; q < kBatch; ++q) v[q] = b + q < b1 ? row[b + q] : 0;
 #pragma unroll
-      for (int q = 0; q < kBatch; ++q) {
-        total += v[q];
-        before += b + q < me ? v[q] : 0;
+        for (int q = 0; q < kBatch; ++q) {
+          total += v[q];
+          before += b + q < me ? v[q] : 0;
+        }
       }
     }
+    for (int o = tpe / 2; o > 0; o >>= 1) {
+      total += __shfl_xor(total, o, kWave);
+      before += __shfl_xor(before, o, kWave);
+    }
+    if (act && sub == 0) {
+      base_s[e] = total;  // the totals first; the scan below turns them into offsets
+      before_s[e] = before;
+    }
   }
-  // Sum over the expert's tpe threads (contiguous lanes of one wave).
-  for (int o = tpe / 2; o > 0; o >>= 1) {
-    total += __shfl_xor(total, o, kWave);
-    before += __shfl_xor(before, o, kWave);
-  }
-  if (act && sub == 0) {
-    base_s[e] = total;  // the totals first; the scan below turns them into offsets
-    before_s[e] = before;
+  // Larger tables: each wave takes experts wid, wid + 4, ...: its 64 lanes
+  // read 64 consecutive block counts of the expert's row per load (whole
+  // cache lines, four experts' loads in flight together), then two wave sums
+  // give the expert's total and the part from the blocks before this one.
+  constexpr int kEx = 4;
+  for (int e0 = WAVE_ROWS ? wid : E; e0 < E; e0 += kCiWaves * kEx) {
+    int total[kEx], before[kEx];
+#pragma unroll
+    for (int x = 0; x < kEx; ++x) total[x] = before[x] = 0;
+    for (int b0 = 0; b0 < nblk; b0 += kWave) {
+      const int b = b0 + lane;
+      int v[kEx];
+#pragma unroll
+      for (int x = 0; x < kEx; ++x) {
+        const int e = e0 + x * kCiWaves;
+        v[x] = (e < E && b < nblk) ? blk_cnt[static_cast<size_t>(e) * nblk + b] : 0;
+      }
+#pragma unroll
+      for (int x = 0; x < kEx; ++x) {
+        total[x] += v[x];
+        before[x] += b < me ? v[x] : 0;
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < kEx; ++x) {
+      const int e = e0 + x * kCiWaves;
+      const int tot = wave_sum_int(total[x]);
+      const int bef = wave_sum_int(before[x]);
+      if (e < E && lane == 0) {
+        base_s[e] = tot;  // the totals first; the scan below turns them into offsets
+        before_s[e] = bef;
+      }
+    }
   }
   __syncthreads();
   // Exclusive scan of the totals over experts (wave 0).
@@ -331,10 +380,16 @@ moe_status count_index_launch(const int32_t* topk_idx, int T, int k, int E, int3
   hipLaunchKernelGGL(ci_count_kernel, dim3(nblk), dim3(kCiBlock), E * sizeof(int32_t), st,
                      topk_idx, static_cast<int>(Tk), E, nblk, blk_cnt);
   if (moe_status s = check_launch("moe_count_index/count")) return s;
-  if (E <= kFusedExperts && static_cast<long long>(E) * nblk <= kFusedTable) {
-    hipLaunchKernelGGL(ci_scan_scatter_kernel, dim3(nblk), dim3(kCiBlock), 0, st, topk_idx,
-                       static_cast<int>(Tk), E, id_bits(E), nblk, blk_cnt, counts, offsets, dest,
-                       src);
+  if (E <= kFusedExperts &&
+      static_cast<long long>(E) * nblk * static_cast<long long>(nblk) <= kFusedReads) {
+    if (static_cast<long long>(E) * nblk <= kThreadRowsTable && E <= kCiBlock)
+      hipLaunchKernelGGL(ci_scan_scatter_kernel<false>, dim3(nblk), dim3(kCiBlock), 0, st,
+                         topk_idx, static_cast<int>(Tk), E, id_bits(E), nblk, blk_cnt, counts,
+                         offsets, dest, src);
+    else
+      hipLaunchKernelGGL(ci_scan_scatter_kernel<true>, dim3(nblk), dim3(kCiBlock), 0, st,
+                         topk_idx, static_cast<int>(Tk), E, id_bits(E), nblk, blk_cnt, counts,
+                         offsets, dest, src);
     return check_launch("moe_count_index/scan+scatter");
   }
   hipLaunchKernelGGL(ci_scan_kernel, dim3(1), dim3(kScanBlock), 0, st, blk_cnt, E, nblk, blk_off,
