@@ -240,7 +240,7 @@ __global__ __launch_bounds__(kCiBlock) void ci_scan_scatter_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
   const int me = static_cast<int>(blockIdx.x);
-  if (!WAVE_ROWS) {
+  if constexpr (!WAVE_ROWS) {
     // Small tables: tpe threads per expert, a power of two <= 64 with
     // E * tpe <= kCiBlock (an expert's threads share a wave), each summing a
     // run of blocks, eight loads in flight at a time.
@@ -273,38 +273,40 @@ __global__ __launch_bounds__(kCiBlock) void ci_scan_scatter_kernel(
       base_s[e] = total;  // the totals first; the scan below turns them into offsets
       before_s[e] = before;
     }
-  }
-  // Larger tables: each wave takes experts wid, wid + 4, ...: its 64 lanes
-  // read 64 consecutive block counts of the expert's row per load (whole
-  // cache lines, four experts' loads in flight together), then two wave sums
-  // give the expert's total and the part from the blocks before this one.
-  constexpr int kEx = 4;
-  for (int e0 = WAVE_ROWS ? wid : E; e0 < E; e0 += kCiWaves * kEx) {
-    int total[kEx], before[kEx];
+  } else {
+    // Larger tables: each wave takes experts wid, wid + 4, ...: its 64 lanes
+    // read 64 consecutive block counts of the expert's row per load (whole
+    // cache lines, four experts' loads in flight together), then two wave
+    // sums give the expert's total and the part from the blocks before this
+    // one.
+    constexpr int kEx = 4;
+    for (int e0 = wid; e0 < E; e0 += kCiWaves * kEx) {
+      int total[kEx], before[kEx];
 #pragma unroll
-    for (int x = 0; x < kEx; ++x) total[x] = before[x] = 0;
-    for (int b0 = 0; b0 < nblk; b0 += kWave) {
-      const int b = b0 + lane;
-      int v[kEx];
+      for (int x = 0; x < kEx; ++x) total[x] = before[x] = 0;
+      for (int b0 = 0; b0 < nblk; b0 += kWave) {
+        const int b = b0 + lane;
+        int v[kEx];
+#pragma unroll
+        for (int x = 0; x < kEx; ++x) {
+          const int e = e0 + x * kCiWaves;
+          v[x] = (e < E && b < nblk) ? blk_cnt[static_cast<size_t>(e) * nblk + b] : 0;
+        }
+#pragma unroll
+        for (int x = 0; x < kEx; ++x) {
+          total[x] += v[x];
+          before[x] += b < me ? v[x] : 0;
+        }
+      }
 #pragma unroll
       for (int x = 0; x < kEx; ++x) {
         const int e = e0 + x * kCiWaves;
-        v[x] = (e < E && b < nblk) ? blk_cnt[static_cast<size_t>(e) * nblk + b] : 0;
-      }
-#pragma unroll
-      for (int x = 0; x < kEx; ++x) {
-        total[x] += v[x];
-        before[x] += b < me ? v[x] : 0;
-      }
-    }
-#pragma unroll
-    for (int x = 0; x < kEx; ++x) {
-      const int e = e0 + x * kCiWaves;
-      const int tot = wave_sum_int(total[x]);
-      const int bef = wave_sum_int(before[x]);
-      if (e < E && lane == 0) {
-        base_s[e] = tot;  // the totals first; the scan below turns them into offsets
-        before_s[e] = bef;
+        const int tot = wave_sum_int(total[x]);
+        const int bef = wave_sum_int(before[x]);
+        if (e < E && lane == 0) {
+          base_s[e] = tot;  // the totals first; the scan below turns them into offsets
+          before_s[e] = bef;
+        }
       }
     }
   }
