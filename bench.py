@@ -108,7 +108,7 @@ def kernel_name(L, call, wl, code, gather=False):
     prod, M, K, N, E = GEMM_CALLS[call](wl)
     plan = L.moe_grouped_gemm_plan(prod, M, K, N, E, code)
     if not plan["mfma"]:
-        return f"gemm_simt_kernel<{prod}, ...>"
+        return f"gemm_f32_kernel<{prod}, ...>"
     out = "float" if prod == 2 or call == "router_fwd" else "unsigned short"
     mode = 0 if prod == 3 else prod
     glu = "true" if prod == 3 else "false"
@@ -587,8 +587,8 @@ def measure(wl, args, detail):
         "kernels": kernels,
     }
     if wl.dtype != "bf16":
-        rec["note"] = ("float32 layer: FMA kernels (no bf16 MFMA path); the bf16 fractions "
-                       "do not apply")
+        rec["note"] = ("float32 layer: float32-MFMA kernels (no bf16 path); the bf16 "
+                       "fractions do not apply")
 
     if detail and not args.overlap_wgrad and not args.graph and not args.no_overlap_variant:
         # The same step with the expert weight-gradient GEMMs on a second

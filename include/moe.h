@@ -224,7 +224,7 @@ moe_status moe_unpermute_bwd(const void* dy, const void* yp,
  *   da or db may be NULL to skip that product; da_add may be NULL.
  *
  * The bf16 path runs on MFMA tiles when K % 8 == 0 and N % 8 == 0; other
- * shapes and float32 run on a tiled FMA kernel.  On the MFMA path every
+ * shapes and float32 run on an LDS-tiled 64x64 kernel on the float32 matrix cores.  On the MFMA path every
  * operand and result pointer must be 16-byte aligned (MOE_ERR_INVALID_ARG
  * otherwise).  ws/ws_bytes: device workspace of at least
  * moe_grouped_gemm_workspace_size() bytes, 16-byte aligned, used by
@@ -241,7 +241,7 @@ size_t moe_grouped_gemm_workspace_size(int M, int K, int N, int E,
  * product: 0 = forward c (moe_grouped_gemm_fwd), 1 = da, 2 = db
  * (moe_grouped_gemm_bwd), 3 = h of moe_grouped_gemm_swiglu_fwd (N = 2F).  Writes the row/column tile sizes, the wavefront
  * grid of a workgroup (waves_m x waves_n), and the number of reduction
- * slices; *mfma = 1 for the bf16 MFMA kernel, 0 for the FMA kernel.  Any
+ * slices; *mfma = 1 for the bf16 MFMA kernel, 0 for the float32-MFMA kernel.  Any
  * output pointer may be NULL.
  */
 moe_status moe_grouped_gemm_plan(int product, int M, int K, int N, int E,

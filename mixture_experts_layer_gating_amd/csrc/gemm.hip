@@ -34,7 +34,9 @@
 // slices (partials in a workspace, summed in slice order).
 //
 // Float32 (and shapes whose K or N is not a multiple of 8) run on a plain
-// LDS-tiled FMA kernel (gemm_simt_kernel) with the same tile resolution.
+// LDS-tiled 64x64 kernel on the float32 matrix cores (gemm_f32_kernel:
+// operands converted to float32 in LDS, v_mfma_f32_32x32x2_f32) with the same
+// tile resolution.
 #include <math.h>
 
 #include <type_traits>
@@ -330,7 +332,7 @@ __device__ bool resolve_tile(const GemmArgs& p, TileInfo& t) {
 // loads for step s + 4 and (at odd s) pair loads for steps s + 3, s + 4 go out
 // then, three and two steps before they are read.
 constexpr int kBK = 32;
-constexpr int kThreads = 256;           // SIMT fallback: 256 threads per block
+constexpr int kThreads = 256;           // float32 kernel: 4 waves per block
 constexpr unsigned kOOB = 0x80000000u;  // buffer offset that is always out of range
 constexpr int kCpolNonTemporal = 2;     // cache-policy operand of buffer stores: nt
 
@@ -1014,7 +1016,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
   }
 }
 
-// ------------------------------------------------------------------ FMA path
+// ------------------------------------------------------------------ float32 path
 template <typename T>
 __device__ __forceinline__ float to_f32(T v);
 template <>
@@ -1030,7 +1032,7 @@ constexpr int kSimtTile = 64;
 constexpr int kSimtBK = 16;
 
 template <int MODE, typename InT, typename OutT>
-__global__ __launch_bounds__(kThreads) void gemm_simt_kernel(GemmArgs p) {
+__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs p) {
   __shared__ float xs[kSimtBK][kSimtTile + 4];
   __shared__ float ys[kSimtBK][kSimtTile + 4];
   TileInfo t;
@@ -1053,12 +1055,14 @@ __global__ __launch_bounds__(kThreads) void gemm_simt_kernel(GemmArgs p) {
     xld = p.K; xolim = p.K; xt = true;
     yld = p.N; yolim = p.N; yt = true;
   }
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  float acc[4][4];
+  // Four waves, each a 32x32 quarter of the 64x64 tile on the float32 matrix
+  // cores (v_mfma_f32_32x32x2_f32: lane l supplies the row (column) l % 32 at
+  // reduction index l / 32 of each operand).
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  const int wm = wv >> 1, wn = wv & 1;
+  f32x16 acc;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
   for (int r0 = t.r_lo; r0 < t.r_hi; r0 += kSimtBK) {
 #pragma unroll
@@ -1082,26 +1086,22 @@ __global__ __launch_bounds__(kThreads) void gemm_simt_kernel(GemmArgs p) {
     }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < kSimtBK; ++kk) {
-      float a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = xs[kk][ty * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = ys[kk][tx * 4 + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    for (int kk = 0; kk < kSimtBK; kk += 2) {
+      const float a = xs[kk + (lane >> 5)][wm * 32 + (lane & 31)];
+      const float b = ys[kk + (lane >> 5)][wn * 32 + (lane & 31)];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
     }
     __syncthreads();
   }
+  // 32x32 accumulator layout: lane l, register r holds row
+  // (r / 4) * 8 + (l / 32) * 4 + r % 4, column l % 32 of the wave's block.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = ty * 4 + i, col = tx * 4 + j;
+  for (int r = 0; r < 16; ++r) {
+    {
+      const int row = wm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      const int col = wn * 32 + (lane & 31);
       const int ra = t.i0 + row, ca = j0 + col;
-      float v = acc[i][j];
+      float v = acc[r];
       if (MODE == kNN) {
         if (ra < t.g1 && ca < p.N) {
           const long long o = static_cast<long long>(ra) * p.N + ca;
@@ -1199,7 +1199,7 @@ Waves waves_of(Cfg c) {
 
 // The MFMA kernels address operands through buffer descriptors with 32-bit
 // byte offsets: every operand (and one expert's weights) stays below 2^31
-// bytes.  Larger shapes take the FMA kernel.
+// bytes.  Larger shapes take the float32 kernel.
 bool mfma_ok(moe_dtype dt, int M, int K, int N) {
   const long long lim = 1ll << 30;  // elements of 2 bytes
   // Tile-relative store offsets (up to 256 rows of a float32 row of K or N
@@ -1276,7 +1276,7 @@ void launch_simt(GemmArgs p, hipStream_t st) {
     upper = (ceil_div(p.M, kSimtTile) + p.E) * p.ntn;
   }
   const long long grid = ceil_div(upper, 8) * 8;
-  hipLaunchKernelGGL((gemm_simt_kernel<MODE, InT, OutT>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((gemm_f32_kernel<MODE, InT, OutT>), dim3(static_cast<unsigned>(grid)),
                      dim3(kThreads), 0, st, p);
 }
 
