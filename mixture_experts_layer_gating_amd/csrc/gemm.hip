@@ -1164,6 +1164,11 @@ Cfg pick_row_cfg(int M, int E, int ncols) {
   if (mean < 96.0) return ncols >= 256 ? Cfg{64, 256} : Cfg{64, 64};
   const long long tiles256 = (ceil_div(M, 256) + E) * ceil_div(ncols, 256);
   if (tiles256 >= 512) return {256, 256};
+  // Fewer 128x128 tiles than compute units (the large-expert router's
+  // logits: 16384 x 128 outputs, 129 tiles) leave most of the chip idle;
+  // 64x64 tiles (several per CU) spread the same work four times wider.
+  const long long tiles128 = (ceil_div(M, 128) + E) * ceil_div(ncols, 128);
+  if (tiles128 < 256) return {64, 64};
   return {128, 128};
 }
 
