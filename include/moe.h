@@ -36,10 +36,14 @@
  *   never reads device memory; on error nothing is enqueued and
  *   moe_last_error() returns a message (thread-local, valid until the next
  *   call on the same thread).  MOE_ERR_HIP reports a failed kernel launch.
- *   Out-of-range expert ids inside device buffers are caller bugs: the
- *   routing and counting kernels clamp them into [0, E), so the results for
- *   those slots are meaningless but every index derived from them stays a
- *   valid row.  Row maps (dest, src) must come from moe_count_index.
+ *   Out-of-range indices inside device buffers (expert ids, row maps, group
+ *   offsets) are caller bugs.  Every kernel that reads one checks its range:
+ *   an expert id is clamped into [0, E), a row outside its array is not
+ *   read (zeros stand in) or not written, a group whose offsets are
+ *   reversed or leave [0, M] is treated as empty.  The results for those
+ *   entries are meaningless, but no access leaves its buffer, and the kernel
+ *   records the event for moe_index_errors().  Row maps (dest, src) should
+ *   come from moe_count_index.
  * - Weight layouts: router wr[d, E]; expert W1[E, d, 2F] (columns [0, F) gate,
  *   [F, 2F) up); expert W2[E, F, d].
  */
@@ -74,6 +78,33 @@ const char* moe_last_error(void);
 
 /* Library version string. */
 const char* moe_version(void);
+
+/*
+ * moe_index_errors -- which range checks on device-side indices have failed
+ * since the record was last cleared.  The pages define no error handling;
+ * this is the debugging aid for the index-range convention above.
+ * *mask receives an OR of:
+ *   MOE_IDXERR_EXPERT  an expert id outside [0, E): forced ids
+ *                      (moe_route_topk), topk_idx (moe_route_topk_bwd,
+ *                      moe_count_index and its no-alloc variant).
+ *   MOE_IDXERR_ROW     a dest entry outside [0, T*k): moe_permute,
+ *                      moe_unpermute, moe_unpermute_bwd.
+ *   MOE_IDXERR_GROUP   a group with offsets[e] > offsets[e+1], or outside
+ *                      [0, M]: every grouped-GEMM entry point.
+ *   MOE_IDXERR_GATHER  a row-map entry x_rows[p] outside [0, x_phys * x_div):
+ *                      the *_gather GEMM entry points.
+ * The record lives on the device (one per GPU, the current device is read)
+ * and every kernel of the library ORs into it.  The call enqueues a copy of
+ * it on `stream` and WAITS for that stream -- the one call of the library
+ * that synchronises; use it in tests and debugging, not in a hot loop.  With
+ * clear != 0 the record is then reset to 0.  Kernels still running on other
+ * streams may add bits at any time.
+ */
+#define MOE_IDXERR_EXPERT 1u
+#define MOE_IDXERR_ROW 2u
+#define MOE_IDXERR_GROUP 4u
+#define MOE_IDXERR_GATHER 8u
+moe_status moe_index_errors(unsigned int* mask, int clear, moe_stream_t stream);
 
 /*
  * moe_route_topk -- expert selection [Summary, Method details / technical
@@ -210,6 +241,8 @@ moe_status moe_unpermute_bwd(const void* dy, const void* yp,
  * e; `offsets` (int32 [E+1], offsets[0] = 0, non-decreasing,
  * offsets[E] <= M) is read ON THE DEVICE, so no host synchronisation is
  * needed between counting and the GEMM.  M is the host-known row count.
+ * A group whose range is reversed or leaves [0, M] is skipped (no rows
+ * computed; zero weight gradient) and recorded (MOE_IDXERR_GROUP).
  *
  * moe_grouped_gemm_fwd:  c[rows e] = a[rows e] @ b[e]
  *   a [M, K] ab_dtype, b [E, K, N] ab_dtype, c [M, N] c_dtype.
@@ -295,7 +328,9 @@ moe_status moe_grouped_gemm_swiglu_fwd(const void* a, const void* b,
  * moe_grouped_gemm_bwd_gather: moe_grouped_gemm_bwd with a gathered (only db
  *   reads a).
  *   x_rows int32 [M] device; every x_rows[p] / x_div (for the rows the
- *   groups cover) must lie in [0, x_phys).  Requires the bf16 MFMA path
+ *   groups cover) must lie in [0, x_phys) (an entry outside [0, x_phys *
+ *   x_div) reads as a zero row and is recorded, MOE_IDXERR_GATHER).
+ *   Requires the bf16 MFMA path
  *   (K and F, or K and N, multiples of 8) and x_phys * K < 2^30;
  *   MOE_ERR_UNSUPPORTED otherwise.  Other arguments, alignment, workspace
  *   and errors as in the plain calls.

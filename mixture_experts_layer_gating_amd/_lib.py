@@ -28,10 +28,14 @@ MOE_BF16 = 1
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 32
 MOE_NOALLOC_SCRATCH_BYTES = 4 << 20
+MOE_IDXERR_EXPERT = 1
+MOE_IDXERR_ROW = 2
+MOE_IDXERR_GROUP = 4
+MOE_IDXERR_GATHER = 8
 
 # Every exported symbol of include/moe.h.
 SYMBOLS = (
-    "moe_last_error", "moe_version", "moe_route_topk", "moe_route_topk_bwd",
+    "moe_last_error", "moe_version", "moe_index_errors", "moe_route_topk", "moe_route_topk_bwd",
     "moe_count_index_workspace_size", "moe_count_index", "moe_count_index_noalloc",
     "moe_permute",
     "moe_unpermute", "moe_unpermute_bwd", "moe_grouped_gemm_workspace_size",
@@ -87,6 +91,7 @@ _z = ctypes.c_size_t
 _SIG = {
     "moe_last_error": ([], ctypes.c_char_p),
     "moe_version": ([], ctypes.c_char_p),
+    "moe_index_errors": ([_p, _i, _p], _i),
     "moe_route_topk": ([_p, _p, _i, _i, _i, _i, _p, _p, _p, _p, _p], _i),
     "moe_route_topk_bwd": ([_p, _p, _p, _i, _i, _i, _i, _p, _i, _p], _i),
     "moe_count_index_workspace_size": ([_i, _i, _i], _z),
@@ -160,6 +165,13 @@ def moe_last_error():
 
 def moe_version():
     return _lib.moe_version().decode()
+
+
+def moe_index_errors(clear=True, stream=None):
+    """MOE_IDXERR_* bits recorded by the kernels (waits for the stream)."""
+    mask = ctypes.c_uint(0)
+    _check(_lib.moe_index_errors(ctypes.byref(mask), 1 if clear else 0, _stream(stream)))
+    return mask.value
 
 
 def moe_route_topk(logits, bias, T, E, k, renorm, forced_idx, topk_idx, topk_w, probs,

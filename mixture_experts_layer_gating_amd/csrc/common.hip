@@ -22,3 +22,18 @@ moe_status check_launch(const char* what) {
 extern "C" const char* moe_last_error(void) { return moe::g_last_error.c_str(); }
 
 extern "C" const char* moe_version(void) { return "moe-mi355x 0.1 (gfx950)"; }
+
+extern "C" moe_status moe_index_errors(unsigned int* mask, int clear, moe_stream_t stream) {
+  using namespace moe;
+  clear_error();
+  MOE_REQUIRE(mask != nullptr, MOE_ERR_INVALID_ARG, "moe_index_errors: null mask");
+  unsigned int bits = 0;
+  hipStream_t st = as_stream(stream);
+  const bool c = clear != 0;
+  if (moe_status s = index_record_route(st, &bits, c)) return s;
+  if (moe_status s = index_record_count(st, &bits, c)) return s;
+  if (moe_status s = index_record_move(st, &bits, c)) return s;
+  if (moe_status s = index_record_gemm(st, &bits, c)) return s;
+  *mask = bits;
+  return MOE_OK;
+}

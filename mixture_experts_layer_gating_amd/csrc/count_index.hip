@@ -40,10 +40,12 @@ inline int num_chunks(long long Tk) { return static_cast<int>((Tk + kCiChunk - 1
 // Expert id of a slot.  Ids outside [0, E) are a caller error (the routing
 // kernel never writes one); they are clamped, so that counts still sum to
 // T*k, dest / src stay a permutation and every row index derived from them
-// stays inside its buffer.
+// stays inside its buffer, and recorded.
 __device__ __forceinline__ int load_id(const int32_t* __restrict__ ids, int s, int E) {
   const int id = ids[s];
-  return id < 0 ? 0 : (id >= E ? E - 1 : id);
+  if (id >= 0 && id < E) return id;
+  note_index_error(MOE_IDXERR_EXPERT);
+  return id < 0 ? 0 : E - 1;
 }
 
 __global__ __launch_bounds__(kCiBlock) void ci_count_kernel(const int32_t* __restrict__ ids,
@@ -436,6 +438,11 @@ moe_status scratch_of_current_device(void** out) {
 }
 
 }  // namespace
+
+moe_status index_record_count(hipStream_t st, unsigned int* bits, bool clear) {
+  return take_index_flags(st, bits, clear);
+}
+
 }  // namespace moe
 
 extern "C" moe_status moe_count_index(const int32_t* topk_idx, int T, int k, int E,

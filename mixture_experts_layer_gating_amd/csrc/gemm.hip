@@ -111,19 +111,30 @@ __device__ __forceinline__ void order_in_group(int local, int te, int ntn, int g
   mt_local = band * group_rows + (w - nt * rows);
 }
 
+// A group whose offsets are reversed or leave [0, M] (a caller error) gets
+// no tiles; every workgroup sees it, and the first thread of each records it.
+__device__ __forceinline__ bool group_ok(int o0, int o1, int M) {
+  return o0 >= 0 && o0 <= o1 && o1 <= M;
+}
+
 template <int BM>
-__device__ RowTile find_row_tile(const int32_t* __restrict__ offsets, int E, int ntn,
+__device__ RowTile find_row_tile(const int32_t* __restrict__ offsets, int E, int M, int ntn,
                                  int group_rows, int lane) {
   constexpr int kHeld = 4;
   const bool held = E <= kHeld * kWave;
   int o0[kHeld], o1[kHeld], tiles[kHeld], incl[kHeld];
   int total = 0;
+  bool bad = false;
   if (held) {
 #pragma unroll
     for (int c = 0; c < kHeld; ++c) {
       const int e = c * kWave + lane;
       o0[c] = e < E ? offsets[e] : 0;
       o1[c] = e < E ? offsets[e + 1] : 0;
+      if (!group_ok(o0[c], o1[c], M)) {
+        bad = true;
+        o0[c] = o1[c] = 0;
+      }
     }
 #pragma unroll
     for (int c = 0; c < kHeld; ++c) {
@@ -138,10 +149,17 @@ __device__ RowTile find_row_tile(const int32_t* __restrict__ offsets, int E, int
     for (int c = 0; c < E; c += kWave) {
       const int e = c + lane;
       int n = 0;
-      if (e < E) n = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+      if (e < E) {
+        const int a0 = offsets[e], a1 = offsets[e + 1];
+        if (group_ok(a0, a1, M))
+          n = (a1 - a0 + BM - 1) / BM;
+        else
+          bad = true;
+      }
       total += wave_sum_int(n);
     }
   }
+  if (__ballot(bad) != 0 && threadIdx.x == 0) note_index_error(MOE_IDXERR_GROUP);
   const long long n_act = static_cast<long long>(total) * ntn;
   const long long per = (n_act + 7) / 8;
   const long long rank = blockIdx.x >> 3;
@@ -175,8 +193,9 @@ __device__ RowTile find_row_tile(const int32_t* __restrict__ offsets, int E, int
     } else {
       for (int c = 0; c < E; c += kWave) {
         const int e = c + lane;
-        const int a0 = e < E ? offsets[e] : 0;
-        const int a1 = e < E ? offsets[e + 1] : 0;
+        int a0 = e < E ? offsets[e] : 0;
+        int a1 = e < E ? offsets[e + 1] : 0;
+        if (!group_ok(a0, a1, M)) a0 = a1 = 0;
         const int n = (a1 - a0 + BM - 1) / BM;
         const int inc = wave_inclusive_scan(n, lane);
         const int excl = carry + inc - n;
@@ -282,6 +301,11 @@ __device__ bool resolve_tile(const GemmArgs& p, TileInfo& t) {
     t.i0 = mt * BM;
     t.g0 = p.offsets[t.e];
     t.g1 = p.offsets[t.e + 1];
+    if (!group_ok(t.g0, t.g1, p.M)) {
+      // No rows: the tile's weight gradient is written as zeros.
+      if (threadIdx.x == 0) note_index_error(MOE_IDXERR_GROUP);
+      t.g0 = t.g1 = 0;
+    }
     const int len = t.g1 - t.g0;
     // Slice s reduces rows [g0 + s*chunk, g0 + (s+1)*chunk), chunk a multiple of 64.
     const int chunk = ((len + p.split - 1) / p.split + 63) / 64 * 64;
@@ -291,7 +315,7 @@ __device__ bool resolve_tile(const GemmArgs& p, TileInfo& t) {
     return true;
   } else {
     const int lane = threadIdx.x & (kWave - 1);
-    const RowTile r = find_row_tile<BM>(p.offsets, p.E, p.ntn, p.row_group, lane);
+    const RowTile r = find_row_tile<BM>(p.offsets, p.E, p.M, p.ntn, p.row_group, lane);
     if (!r.found) return false;
     t.e = r.e;
     t.g0 = r.g0;
@@ -441,8 +465,10 @@ struct DmaLoader {
   // tile's reduction range, the row map, and a ring of the physical rows of
   // the next four calls (slot = call index % 4).
   int grow[GX && STRIDED ? kPerWave : 1];
-  int g_lo, g_hi, g_div, g_shift;
+  int g_lo, g_hi, g_div, g_shift, g_phys;
   unsigned g_magic;
+  unsigned g_lim;  // row-map entries must lie below this (x_phys * x_div)
+  bool g_bad;      // this lane met a row-map entry outside [0, g_lim)
   unsigned ld_bytes;
   __amdgpu_buffer_rsrc_t g_rs;  // the row map
   int ring[GX && STRIDED ? kPerWave : 1][4];
@@ -450,6 +476,15 @@ struct DmaLoader {
   __device__ __forceinline__ void init(const Operand& op, int r_lo, int r_hi) {
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
+    g_bad = false;
+    if constexpr (GX) {
+      // An entry at or past x_phys * x_div (or negative) is a caller error:
+      // its row reads as zeros (physical row x_phys, just past the range)
+      // and is recorded.
+      const long long lim = static_cast<long long>(op.phys) * op.rdiv;
+      g_lim = static_cast<unsigned>(lim < 0x80000000LL ? lim : 0x80000000LL);
+      g_phys = op.phys;
+    }
 #pragma unroll
     for (int q = 0; q < kPerWave; ++q) {
       const int cid = q * NW + w;  // 1 KB piece of the buffer
@@ -466,7 +501,18 @@ struct DmaLoader {
         const int room = r_hi - r_lo - c * 8 - 8;
         klim = room >= 0 ? room / kSpan + 1 : 0;
         int prow = row;  // physical row
-        if constexpr (GX) prow = row < op.o_valid ? div_rows(op.rows[row], op.rdiv, op.rmagic) : 0;
+        if constexpr (GX) {
+          prow = 0;
+          if (row < op.o_valid) {
+            const int raw = op.rows[row];
+            if (static_cast<unsigned>(raw) < g_lim) {
+              prow = div_rows(raw, op.rdiv, op.rmagic);
+            } else {
+              prow = op.phys;
+              g_bad = true;
+            }
+          }
+        }
         voff[q] = row < op.o_valid ? static_cast<unsigned>((prow * op.ld + c * 8) * 2) : kOOB;
       } else {
         // Rows past the reduction range fall outside the buffer range; so do
@@ -538,12 +584,24 @@ struct DmaLoader {
   // the loads.
   __device__ __forceinline__ void prepare(int sl) {
     if constexpr (GX && STRIDED) {
+      // Entries out of range become row g_phys, whose loads fall past the
+      // buffer range (zeros).
       if (g_shift >= 0) {  // uniform: a power-of-two divisor is a shift
 #pragma unroll
-        for (int q = 0; q < kPerWave; ++q) ring[q][sl] = ring[q][sl] >> g_shift;
+        for (int q = 0; q < kPerWave; ++q) {
+          const unsigned raw = static_cast<unsigned>(ring[q][sl]);
+          const bool ok = raw < g_lim;
+          g_bad |= !ok;
+          ring[q][sl] = ok ? static_cast<int>(raw >> g_shift) : g_phys;
+        }
       } else {
 #pragma unroll
-        for (int q = 0; q < kPerWave; ++q) ring[q][sl] = div_rows(ring[q][sl], g_div, g_magic);
+        for (int q = 0; q < kPerWave; ++q) {
+          const unsigned raw = static_cast<unsigned>(ring[q][sl]);
+          const bool ok = raw < g_lim;
+          g_bad |= !ok;
+          ring[q][sl] = ok ? div_rows(static_cast<int>(raw), g_div, g_magic) : g_phys;
+        }
       }
       // Pin the results here: otherwise the compiler sinks the division to
       // just before the load that uses it, after the step's barrier.
@@ -894,6 +952,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
       MOE_REDUCE(0);
     }
 #undef MOE_REDUCE
+  }
+  if constexpr (GX) {
+    if (__ballot(xl.g_bad) != 0 && lane == 0) note_index_error(MOE_IDXERR_GATHER);
   }
 
   if constexpr (GLU) {
@@ -1328,6 +1389,11 @@ moe_status check_gemm(const void* offsets, int M, int K, int N, int E, moe_dtype
 }
 
 }  // namespace
+
+moe_status index_record_gemm(hipStream_t st, unsigned int* bits, bool clear) {
+  return take_index_flags(st, bits, clear);
+}
+
 }  // namespace moe
 
 using namespace moe;

@@ -33,6 +33,41 @@ inline hipStream_t as_stream(moe_stream_t s) {
   return reinterpret_cast<hipStream_t>(s);
 }
 
+// ---------------------------------------------------------------- index record
+// Out-of-range indices met by this translation unit's kernels: MOE_IDXERR_*
+// bits, OR-ed in by the kernel that met one.  Each unit (and each device) has
+// its own copy; moe_index_errors reads and clears them all.
+[[maybe_unused]] static __device__ unsigned int g_index_flags;
+
+__device__ __forceinline__ void note_index_error(unsigned int bits) {
+  atomicOr(&g_index_flags, bits);
+}
+
+// Host side: this unit's record on the current device, copied on `st`, which
+// is then waited for; cleared afterwards when `clear` is set.
+[[maybe_unused]] static moe_status take_index_flags(hipStream_t st, unsigned int* bits,
+                                                    bool clear) {
+  unsigned int v = 0;
+  hipError_t e =
+      hipMemcpyFromSymbolAsync(&v, HIP_SYMBOL(g_index_flags), sizeof v, 0, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e == hipSuccess && clear && v != 0) {
+    static const unsigned int zero = 0;
+    e = hipMemcpyToSymbolAsync(HIP_SYMBOL(g_index_flags), &zero, sizeof zero, 0,
+                               hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+  }
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, std::string("moe_index_errors: ") + hipGetErrorString(e));
+  *bits |= v;
+  return MOE_OK;
+}
+
+// The units whose kernels read indices from caller buffers.
+moe_status index_record_route(hipStream_t st, unsigned int* bits, bool clear);
+moe_status index_record_count(hipStream_t st, unsigned int* bits, bool clear);
+moe_status index_record_move(hipStream_t st, unsigned int* bits, bool clear);
+moe_status index_record_gemm(hipStream_t st, unsigned int* bits, bool clear);
+
 inline size_t dtype_size(moe_dtype t) { return t == MOE_BF16 ? 2 : 4; }
 inline bool dtype_ok(moe_dtype t) { return t == MOE_F32 || t == MOE_BF16; }
 

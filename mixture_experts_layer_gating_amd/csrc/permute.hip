@@ -68,6 +68,12 @@ struct Chunk<float> {
   }
 };
 
+// A dest entry names a row of the T*k-row permuted array; one outside it
+// (a caller error) is neither read nor written, and is recorded.
+__device__ __forceinline__ bool row_ok(int d, unsigned rows) {
+  return static_cast<unsigned>(d) < rows;
+}
+
 // xp[dest[t*k + j], :] = x[t, :] for every slot (t, j): each token row is
 // read once and written to its k rows (the same result as gathering
 // xp[p] = x[src[p] / k]).  One workgroup per token row, threads on
@@ -78,14 +84,23 @@ __global__ __launch_bounds__(kMoveBlock) void permute_kernel(const char* __restr
                                                              int Tn, int k, int chunks_per_row,
                                                              char* __restrict__ xp) {
   const size_t row_bytes = static_cast<size_t>(chunks_per_row) * 16;
+  const unsigned rows = static_cast<unsigned>(Tn) * static_cast<unsigned>(k);
+  bool bad = false;
   for (int t = blockIdx.x; t < Tn; t += gridDim.x) {
     const char* in = x + static_cast<size_t>(t) * row_bytes;
     const int32_t* drow = dest + static_cast<size_t>(t) * k;
     for (int c = threadIdx.x; c < chunks_per_row; c += kMoveBlock) {
       const Vec16 v = ld16_stream(in + c * 16);
-      for (int j = 0; j < k; ++j) st16(xp + static_cast<size_t>(drow[j]) * row_bytes + c * 16, v);
+      for (int j = 0; j < k; ++j) {
+        const int d = drow[j];
+        if (row_ok(d, rows))
+          st16(xp + static_cast<size_t>(d) * row_bytes + c * 16, v);
+        else
+          bad = true;
+      }
     }
   }
+  if (bad) note_index_error(MOE_IDXERR_ROW);
 }
 
 constexpr int kUnroll = 8;  // slots whose loads are issued together
@@ -101,6 +116,8 @@ __global__ __launch_bounds__(kMoveBlock) void unpermute_kernel(const char* __res
                                                                char* __restrict__ y) {
   constexpr int N = Chunk<T>::N;
   const size_t row_bytes = static_cast<size_t>(chunks_per_row) * 16;
+  const unsigned rows = static_cast<unsigned>(Tn) * static_cast<unsigned>(k);
+  bool bad = false;
   for (int t = blockIdx.x; t < Tn; t += gridDim.x) {
     const int32_t* drow = dest + static_cast<size_t>(t) * k;
     const float* wrow = w ? w + static_cast<size_t>(t) * k : nullptr;
@@ -111,9 +128,16 @@ __global__ __launch_bounds__(kMoveBlock) void unpermute_kernel(const char* __res
       for (int j0 = 0; j0 < k; j0 += kUnroll) {
         Vec16 raw[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-          if (j0 + u < k)
-            raw[u] = ld16_stream(yp + static_cast<size_t>(drow[j0 + u]) * row_bytes + c * 16);
+        for (int u = 0; u < kUnroll; ++u) {
+          if (j0 + u < k) {
+            // An out-of-range row reads row 0 and contributes zeros.
+            const int d = drow[j0 + u];
+            const bool ok = row_ok(d, rows);
+            bad |= !ok;
+            raw[u] = ld16_stream(yp + static_cast<size_t>(ok ? d : 0) * row_bytes + c * 16);
+            if (!ok) raw[u] = Vec16{};
+          }
+        }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
           if (j0 + u < k) {
@@ -128,14 +152,15 @@ __global__ __launch_bounds__(kMoveBlock) void unpermute_kernel(const char* __res
       st16(y + static_cast<size_t>(t) * row_bytes + c * 16, Chunk<T>::pack(acc));
     }
   }
+  if (bad) note_index_error(MOE_IDXERR_ROW);
 }
 
 // One block per token: dyp rows of its k slots and the k dot products dw.
 template <typename T>
 __global__ __launch_bounds__(kMoveBlock) void unpermute_bwd_kernel(
     const char* __restrict__ dy, const char* __restrict__ yp, const int32_t* __restrict__ dest,
-    const float* __restrict__ w, int k, int chunks_per_row, char* __restrict__ dyp,
-    float* __restrict__ dw) {
+    const float* __restrict__ w, int k, unsigned rows, int chunks_per_row,
+    char* __restrict__ dyp, float* __restrict__ dw) {
   constexpr int N = Chunk<T>::N;
   __shared__ float part[kMoveBlock / kWave][MOE_MAX_TOPK];
   const int t = blockIdx.x;
@@ -148,6 +173,7 @@ __global__ __launch_bounds__(kMoveBlock) void unpermute_bwd_kernel(
   float dot[MOE_MAX_TOPK];
 #pragma unroll
   for (int j = 0; j < MOE_MAX_TOPK; ++j) dot[j] = 0.f;
+  bool bad = false;
   for (int c = threadIdx.x; c < chunks_per_row; c += kMoveBlock) {
     float g[N];
     Chunk<T>::unpack(ld16_stream(dyrow + c * 16), g);
@@ -155,10 +181,20 @@ __global__ __launch_bounds__(kMoveBlock) void unpermute_bwd_kernel(
     for (int j0 = 0; j0 < MOE_MAX_TOPK; j0 += kUnroll) {
       if (j0 >= k) break;
       Vec16 raw[kUnroll];
+      int dd[kUnroll];
+      bool ok[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-        if (j0 + u < k)
-          raw[u] = ld16_stream(yp + static_cast<size_t>(drow[j0 + u]) * row_bytes + c * 16);
+      for (int u = 0; u < kUnroll; ++u) {
+        if (j0 + u < k) {
+          // An out-of-range row is not written and reads as zeros (dw gets
+          // nothing from it).
+          dd[u] = drow[j0 + u];
+          ok[u] = row_ok(dd[u], rows);
+          bad |= !ok[u];
+          raw[u] = ld16_stream(yp + static_cast<size_t>(ok[u] ? dd[u] : 0) * row_bytes + c * 16);
+          if (!ok[u]) raw[u] = Vec16{};
+        }
+      }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         if (j0 + u < k) {
@@ -170,11 +206,12 @@ __global__ __launch_bounds__(kMoveBlock) void unpermute_bwd_kernel(
             dot[j0 + u] = fmaf(g[q], v[q], dot[j0 + u]);
             o[q] = wt * g[q];
           }
-          st16(dyp + static_cast<size_t>(drow[j0 + u]) * row_bytes + c * 16, Chunk<T>::pack(o));
+          if (ok[u]) st16(dyp + static_cast<size_t>(dd[u]) * row_bytes + c * 16, Chunk<T>::pack(o));
         }
       }
     }
   }
+  if (bad) note_index_error(MOE_IDXERR_ROW);
 #pragma unroll
   for (int j = 0; j < MOE_MAX_TOPK; ++j) {
     if (j < k) {
@@ -209,6 +246,11 @@ moe_status check_move(int T, int k, int d, moe_dtype dt) {
 }
 
 }  // namespace
+
+moe_status index_record_move(hipStream_t st, unsigned int* bits, bool clear) {
+  return take_index_flags(st, bits, clear);
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -248,13 +290,16 @@ extern "C" moe_status moe_unpermute_bwd(const void* dy, const void* yp, const in
   MOE_REQUIRE(dy && yp && dest && w && dyp && dw, MOE_ERR_INVALID_ARG,
               "moe_unpermute_bwd: null pointer");
   const int cpr = static_cast<int>(d * dtype_size(dtype) / 16);
+  const unsigned rows = static_cast<unsigned>(T) * static_cast<unsigned>(k);
   if (dtype == MOE_BF16)
     hipLaunchKernelGGL(unpermute_bwd_kernel<uint16_t>, dim3(T), dim3(kMoveBlock), 0,
                        as_stream(stream), static_cast<const char*>(dy),
-                       static_cast<const char*>(yp), dest, w, k, cpr, static_cast<char*>(dyp), dw);
+                       static_cast<const char*>(yp), dest, w, k, rows, cpr,
+                       static_cast<char*>(dyp), dw);
   else
     hipLaunchKernelGGL(unpermute_bwd_kernel<float>, dim3(T), dim3(kMoveBlock), 0,
                        as_stream(stream), static_cast<const char*>(dy),
-                       static_cast<const char*>(yp), dest, w, k, cpr, static_cast<char*>(dyp), dw);
+                       static_cast<const char*>(yp), dest, w, k, rows, cpr,
+                       static_cast<char*>(dyp), dw);
   return check_launch("moe_unpermute_bwd");
 }

@@ -38,10 +38,13 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
 // any expert's).
 constexpr int kNoExpert = 0x7fffffff;
 
-// A forced expert id outside [0, E) is a caller error; it is clamped so that
-// no read or row index derived from it leaves its buffer.
+// An expert id read from a caller's buffer (forced ids, the backward pass's
+// topk_idx) outside [0, E) is a caller error; it is clamped so that no read
+// or row index derived from it leaves its buffer, and recorded.
 __device__ __forceinline__ int clamp_expert(int e, int E) {
-  return e < 0 ? 0 : (e >= E ? E - 1 : e);
+  if (e >= 0 && e < E) return e;
+  note_index_error(MOE_IDXERR_EXPERT);
+  return e < 0 ? 0 : E - 1;
 }
 
 template <int EPL>
@@ -289,7 +292,7 @@ __global__ __launch_bounds__(kRouteBlock) void route_topk_bwd_kernel(
   int my_id = 0;
   float my_p = 0.f, my_dw = 0.f;
   if (lane < k) {
-    my_id = irow[lane];
+    my_id = clamp_expert(irow[lane], E);
     my_p = prow[my_id];
     my_dw = drow[lane];
   }
@@ -423,3 +426,9 @@ extern "C" moe_status moe_route_topk_bwd(const float* probs, const int32_t* topk
     launch_route_bwd<16>(T, grid, st, probs, topk_idx, dtopk_w, E, k, renorm, dlogits, dlogits_dtype);
   return check_launch("moe_route_topk_bwd");
 }
+
+namespace moe {
+moe_status index_record_route(hipStream_t st, unsigned int* bits, bool clear) {
+  return take_index_flags(st, bits, clear);
+}
+}  // namespace moe

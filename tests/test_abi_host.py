@@ -34,6 +34,18 @@ def test_version_and_error_string():
     assert isinstance(L.moe_last_error(), str)
 
 
+def test_index_error_bits_match_header():
+    text = open(HEADER).read()
+    bits = {m.group(1): int(m.group(2)) for m in
+            re.finditer(r"#define (MOE_IDXERR_[A-Z]+) (\d+)u", text)}
+    assert bits == {n: getattr(L, n) for n in
+                    ("MOE_IDXERR_EXPERT", "MOE_IDXERR_ROW", "MOE_IDXERR_GROUP", "MOE_IDXERR_GATHER")}
+    assert len(set(bits.values())) == 4 and all(v & (v - 1) == 0 for v in bits.values())
+    # A null mask is refused on the host, before any device work.
+    assert _rc("moe_index_errors", None, 1, None) == L.MOE_ERR_INVALID_ARG
+    assert "mask" in L.moe_last_error()
+
+
 def _rc(name, *args):
     return getattr(L.lib(), name)(*args)
 
