@@ -659,27 +659,50 @@ def measure(wl, args, detail):
     return rec, inp
 
 
-def library_gemm_reference(torch):
+def library_gemm_reference(torch, own=True):
     """What a plain library GEMM (torch.matmul, hipBLASLt) sustains on this
-    box for a large square bf16 product: context for the MFMA roofline."""
+    box for a large square bf16 product: context for the MFMA roofline.  With
+    ``own``, this library's grouped GEMM runs the same product as a single
+    group (the forward NN kernel, and the NT kernel of the data gradient), so
+    the two kernels are compared on a shape with no expert structure."""
     dev = torch.device("cuda:0")
     n = 8192
     ga = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
     gb = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
-    for _ in range(3):
-        torch.matmul(ga, gb)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(10):
-        torch.matmul(ga, gb)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / 10
+
+    def tflops(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return 2 * n ** 3 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12
+
+    lib = tflops(lambda: torch.matmul(ga, gb))
+    res = {"what": "torch.matmul (hipBLASLt) bf16 8192 x 8192 x 8192",
+           "tflops": round(lib, 1), "frac_of_peak": round(lib / PEAK_BF16_TFLOPS, 4)}
+    if own:
+        import mixture_experts_layer_gating_amd._lib as L
+        off = torch.tensor([0, n], dtype=torch.int32, device=dev)
+        gc_ = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+        b3 = gb.view(1, n, n)
+        nn = tflops(lambda: L.moe_grouped_gemm_fwd(ga, b3, off, n, n, n, 1, L.MOE_BF16, gc_,
+                                                   L.MOE_BF16))
+        nt = tflops(lambda: L.moe_grouped_gemm_bwd(None, b3, ga, off, n, n, n, 1, L.MOE_BF16,
+                                                   gc_, None, None, None, 0))
+        res["this_library_one_group"] = {
+            "what": "moe_grouped_gemm_fwd (NN) and moe_grouped_gemm_bwd data gradient (NT), "
+                    "one group, bf16 8192 x 8192 x 8192",
+            "nn_tflops": round(nn, 1), "nt_tflops": round(nt, 1),
+            "nn_frac_of_peak": round(nn / PEAK_BF16_TFLOPS, 4),
+            "nt_frac_of_peak": round(nt / PEAK_BF16_TFLOPS, 4)}
+        del gc_
     del ga, gb
-    return {"what": "torch.matmul (hipBLASLt) bf16 8192 x 8192 x 8192",
-            "tflops": round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1),
-            "frac_of_peak": round(2 * n ** 3 / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    return res
 
 
 # ---------------------------------------------------------------- main
@@ -704,6 +727,9 @@ def main():
                     help="skip the two-stream variant of the headline workload (profiling "
                          "runs: overlapped kernels stretch each other's durations)")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--no-own-dense", action="store_true",
+                    help="leave this library's one-group GEMMs out of the library reference "
+                         "(profiling passes: they would add dispatches to the expert kernels)")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="write a text summary of a rocprofv3 --kernel-trace --stats output")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -755,7 +781,8 @@ def main():
         return cpu_baseline(inp, tokens)
 
     head, inp = measure(wl, args, detail=True)
-    ref_gemm = library_gemm_reference(torch) if wl.dtype == "bf16" else None
+    ref_gemm = (library_gemm_reference(torch, own=not args.no_own_dense)
+                if wl.dtype == "bf16" else None)
     head_cpu = cpu_leg(inp, args.cpu_tokens or CPU_TOKENS.get(wl.name, 1024))
     del inp
     configs = {}

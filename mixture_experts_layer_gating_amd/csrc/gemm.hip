@@ -468,7 +468,8 @@ struct DmaLoader {
   int g_lo, g_hi, g_div, g_shift, g_phys;
   unsigned g_magic;
   unsigned g_lim;  // row-map entries must lie below this (x_phys * x_div)
-  bool g_bad;      // this lane met a row-map entry outside [0, g_lim)
+  bool g_bad;      // k-contiguous: this lane met a row-map entry outside [0, g_lim)
+  uint64_t g_badmask;  // k-strided: OR of the lane masks of bad entries (wave-uniform)
   unsigned ld_bytes;
   __amdgpu_buffer_rsrc_t g_rs;  // the row map
   int ring[GX && STRIDED ? kPerWave : 1][4];
@@ -477,6 +478,7 @@ struct DmaLoader {
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
     g_bad = false;
+    g_badmask = 0;
     if constexpr (GX) {
       // An entry at or past x_phys * x_div (or negative) is a caller error:
       // its row reads as zeros (physical row x_phys, just past the range)
@@ -585,22 +587,26 @@ struct DmaLoader {
   __device__ __forceinline__ void prepare(int sl) {
     if constexpr (GX && STRIDED) {
       // Entries out of range become row g_phys, whose loads fall past the
-      // buffer range (zeros).
+      // buffer range (zeros); a wave-wide mask of such lanes is kept in
+      // scalar registers for the record.  With a shift the clamp is a minimum: a valid entry
+      // (below g_phys << g_shift) shifts to below g_phys, a larger one to at
+      // least g_phys, a negative one (arithmetic shift) to a negative value,
+      // i.e. a large unsigned one.
       if (g_shift >= 0) {  // uniform: a power-of-two divisor is a shift
 #pragma unroll
         for (int q = 0; q < kPerWave; ++q) {
-          const unsigned raw = static_cast<unsigned>(ring[q][sl]);
-          const bool ok = raw < g_lim;
-          g_bad |= !ok;
-          ring[q][sl] = ok ? static_cast<int>(raw >> g_shift) : g_phys;
+          const unsigned sh = static_cast<unsigned>(ring[q][sl] >> g_shift);
+          const unsigned prow = min(sh, static_cast<unsigned>(g_phys));
+          g_badmask |= __ballot(prow == static_cast<unsigned>(g_phys));
+          ring[q][sl] = static_cast<int>(prow);
         }
       } else {
 #pragma unroll
         for (int q = 0; q < kPerWave; ++q) {
           const unsigned raw = static_cast<unsigned>(ring[q][sl]);
-          const bool ok = raw < g_lim;
-          g_bad |= !ok;
-          ring[q][sl] = ok ? div_rows(static_cast<int>(raw), g_div, g_magic) : g_phys;
+          const int prow = raw < g_lim ? div_rows(static_cast<int>(raw), g_div, g_magic) : g_phys;
+          g_badmask |= __ballot(prow == g_phys);
+          ring[q][sl] = prow;
         }
       }
       // Pin the results here: otherwise the compiler sinks the division to
@@ -954,7 +960,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
 #undef MOE_REDUCE
   }
   if constexpr (GX) {
-    if (__ballot(xl.g_bad) != 0 && lane == 0) note_index_error(MOE_IDXERR_GATHER);
+    if ((__ballot(xl.g_bad) | xl.g_badmask) != 0 && lane == 0) note_index_error(MOE_IDXERR_GATHER);
   }
 
   if constexpr (GLU) {
