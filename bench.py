@@ -53,11 +53,15 @@ def log(*a):
 
 
 # ---------------------------------------------------------------- work model
-def call_work(wl, b):
+def call_work(wl, b, gather_dy=False):
     """Algorithmic FLOPs and HBM bytes of each library call of one step.
 
     Bytes count each input read once and each output written once (``b`` =
-    bytes per activation / weight element; indices and gate values 4 B)."""
+    bytes per activation / weight element; indices and gate values 4 B).  A
+    gathered operand counts as its permuted copy would (T*k rows).  With
+    ``gather_dy`` the combine's backward writes no dyp, GEMM 2's backward
+    reads dy through the row map with the sorted gate weights, and the SwiGLU
+    backward also writes the scaled activation."""
     T, d, E, k, F = wl.T, wl.d, wl.E, wl.k, wl.F
     Tk = T * k
     f = {}
@@ -81,6 +85,12 @@ def call_work(wl, b):
     f["route_topk_bwd"] = (0, T * E * 4 + Tk * 8 + T * E * b)
     f["router_bwd_da"] = (2 * T * E * d, T * E * b + d * E * b + 2 * T * d * b)
     f["router_bwd_dw"] = (2 * T * d * E, T * d * b + T * E * b + d * E * 4)
+    if gather_dy:
+        f["unpermute_bwd"] = (0, T * d * b + Tk * d * b + Tk * 12)
+        f["gather_scale"] = (0, Tk * 12)
+        f["gemm2_bwd_da"] = (f["gemm2_bwd_da"][0], f["gemm2_bwd_da"][1] + Tk * 8)
+        f["gemm2_bwd_dw"] = (f["gemm2_bwd_dw"][0], f["gemm2_bwd_dw"][1] + Tk * 4)
+        f["act_bwd"] = (0, f["act_bwd"][1] + Tk * F * b + Tk * 4)
     return f
 
 
@@ -103,7 +113,7 @@ MOVE_CALLS = ("unpermute", "unpermute_bwd", "act_bwd", "permute_bwd")  # HBM-bou
 GATHER_CALLS = ("gemm1_swiglu_fwd", "gemm1_bwd_dw")  # read x through src / k when gathering
 
 
-def kernel_name(L, call, wl, code, gather=False):
+def kernel_name(L, call, wl, code, gather=False, gather_dy=False):
     """Name (as rocprofv3 prints it) of the kernel a GEMM call launches."""
     prod, M, K, N, E = GEMM_CALLS[call](wl)
     plan = L.moe_grouped_gemm_plan(prod, M, K, N, E, code)
@@ -112,9 +122,17 @@ def kernel_name(L, call, wl, code, gather=False):
     out = "float" if prod == 2 or call == "router_fwd" else "unsigned short"
     mode = 0 if prod == 3 else prod
     glu = "true" if prod == 3 else "false"
-    gx = "true" if gather and call in GATHER_CALLS else "false"
+    gx = "true" if ((gather and call in GATHER_CALLS)
+                    or (gather_dy and call == "gemm2_bwd_da")) else "false"
+    gy = "true" if gather_dy and call == "gemm2_bwd_dw" else "false"
     return (f"gemm_mfma_kernel<{mode}, {plan['tile_m']}, {plan['tile_n']}, "
-            f"{plan['waves_m']}, {plan['waves_n']}, {out}, {glu}, {gx}>")
+            f"{plan['waves_m']}, {plan['waves_n']}, {out}, {glu}, {gx}, {gy}>")
+
+
+def default_gather_dy(L, wl, code):
+    """Whether the layer reads dy through the row map in GEMM 2's backward
+    (its default wherever the bf16 MFMA path applies)."""
+    return bool(L.moe_grouped_gemm_plan(1, wl.T * wl.k, wl.F, wl.d, wl.E, code)["mfma"])
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -261,7 +279,9 @@ def summarize_pmc(fetch_dir, write_dir, out, command, command2, workload):
     f_write = gib_kib / (sum(cw) / len(cw))
     sha = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
     wl = WORKLOADS[workload]
-    work = call_work(wl, 2 if wl.dtype == "bf16" else 4)
+    import mixture_experts_layer_gating_amd._lib as L
+    code = L.MOE_BF16 if wl.dtype == "bf16" else L.MOE_F32
+    work = call_work(wl, 2 if wl.dtype == "bf16" else 4, default_gather_dy(L, wl, code))
     lines = [f"# HBM traffic of the grouped-GEMM kernels (rocprofv3 --pmc), workload {workload}",
              "",
              f"command (FETCH_SIZE pass): {command}",
@@ -301,10 +321,11 @@ def _kernel_calls(wl):
     code = L.MOE_BF16 if wl.dtype == "bf16" else L.MOE_F32
     plan = L.moe_grouped_gemm_plan(3, wl.T * wl.k, wl.d, 2 * wl.F, wl.E, code)
     gather = bool(plan["mfma"])
+    gdy = default_gather_dy(L, wl, code)
     calls = [c for c in GEMM_CALLS if c not in ("gemm1_fwd",)]
     out = {}
     for c in calls:
-        out.setdefault(kernel_name(L, c, wl, code, gather), []).append(c)
+        out.setdefault(kernel_name(L, c, wl, code, gather, gdy), []).append(c)
     return out
 
 
@@ -328,7 +349,8 @@ def summarize_busy(directory, trace_dir, out, command, command_trace, workload):
     for r in _csv_rows(trace_dir, "_kernel_stats.csv"):
         durs[_short(r["Name"])] = float(r["AverageNs"])
     wl = WORKLOADS[workload]
-    work = call_work(wl, 2)
+    import mixture_experts_layer_gating_amd._lib as L
+    work = call_work(wl, 2, default_gather_dy(L, wl, L.MOE_BF16))
     names = _kernel_calls(wl)
     lines = [f"# Clock and MFMA activity of the grouped-GEMM kernels, workload {workload}", "",
              f"command (--pmc pass): {command}",
@@ -456,8 +478,9 @@ def measure(wl, args, detail):
     bias = None if inp.bias is None else torch.from_numpy(inp.bias).to(dev)
     forced = None if inp.forced_idx is None else torch.from_numpy(inp.forced_idx).to(dev)
     layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, dtype=tdt, device=dev,
-                     overlap_wgrad=args.overlap_wgrad and detail)
-    work = call_work(wl, b)
+                     overlap_wgrad=args.overlap_wgrad and detail,
+                     gather_dy=not args.no_gather_dy)
+    work = call_work(wl, b, layer.gather_dy)
 
     def step():
         layer.forward(x, wr, w1, w2, bias=bias, forced_idx=forced)
@@ -475,7 +498,8 @@ def measure(wl, args, detail):
     torch.cuda.synchronize()
     layer.timer = None
     warm_ms = warm.per_call_ms()
-    kname = {n: kernel_name(L, n, wl, code, layer.gather_x) for n in GEMM_CALLS if n in warm_ms}
+    kname = {n: kernel_name(L, n, wl, code, layer.gather_x, layer.gather_dy)
+             for n in GEMM_CALLS if n in warm_ms}
     by_kernel = {}
     for n, kn in kname.items():
         by_kernel.setdefault(kn, []).append(n)
@@ -563,7 +587,7 @@ def measure(wl, args, detail):
             rec["gbs"] = round(by / (avg * 1e-3) / 1e9, 1)
             rec["frac_hbm"] = round(by / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
         if name in GEMM_CALLS:
-            rec["kernel"] = kernel_name(L, name, wl, code, layer.gather_x)
+            rec["kernel"] = kernel_name(L, name, wl, code, layer.gather_x, layer.gather_dy)
         kernels[name] = rec
 
     # Grouped-GEMM share of the bf16 peak, over the six expert GEMM launches.
@@ -727,6 +751,9 @@ def main():
                     help="skip the two-stream variant of the headline workload (profiling "
                          "runs: overlapped kernels stretch each other's durations)")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--no-gather-dy", action="store_true",
+                    help="write the combine's gradient dyp and run GEMM 2's backward on it "
+                         "(MoELayer(gather_dy=False)) instead of reading dy through the row map")
     ap.add_argument("--no-own-dense", action="store_true",
                     help="leave this library's one-group GEMMs out of the library reference "
                          "(profiling passes: they would add dispatches to the expert kernels)")

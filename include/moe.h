@@ -88,11 +88,12 @@ const char* moe_version(void);
  *                      (moe_route_topk), topk_idx (moe_route_topk_bwd,
  *                      moe_count_index and its no-alloc variant).
  *   MOE_IDXERR_ROW     a dest entry outside [0, T*k): moe_permute,
- *                      moe_unpermute, moe_unpermute_bwd.
+ *                      moe_unpermute, moe_unpermute_bwd; a src entry
+ *                      outside [0, n): moe_gather_scale.
  *   MOE_IDXERR_GROUP   a group with offsets[e] > offsets[e+1], or outside
  *                      [0, M]: every grouped-GEMM entry point.
- *   MOE_IDXERR_GATHER  a row-map entry x_rows[p] outside [0, x_phys * x_div):
- *                      the *_gather GEMM entry points.
+ *   MOE_IDXERR_GATHER  a row-map entry outside [0, phys * div): the
+ *                      *_gather GEMM entry points.
  * The record lives on the device (one per GPU, the current device is read)
  * and every kernel of the library ORs into it.  The call enqueues a copy of
  * it on `stream` and WAITS for that stream -- the one call of the library
@@ -226,6 +227,9 @@ moe_status moe_unpermute(const void* yp, const int32_t* dest, const float* w,
  * dw[t, j] = sum_i dy[t, i] * yp[dest[t*k+j], i]   (float32).
  *   dy [T, d], yp [T*k, d], dyp [T*k, d]: `dtype`.  w [T, k] float32, in.
  *   dw [T, k] float32, out.  Requires d % 8 == 0.
+ *   dyp may be NULL: only dw is computed (the path in which GEMM 2's
+ *   backward reads dy through the row map instead, see
+ *   moe_grouped_gemm_bwd_scaled_gather).
  */
 moe_status moe_unpermute_bwd(const void* dy, const void* yp,
                              const int32_t* dest, const float* w, int T, int k,
@@ -349,6 +353,45 @@ moe_status moe_grouped_gemm_bwd_gather(const void* a, const int32_t* a_rows,
                                        moe_stream_t stream);
 
 /*
+ * moe_gather_scale -- the gate weights in expert-sorted row order:
+ * out[p] = w[src[p]] for p < n (w and src as from moe_route_topk and
+ * moe_count_index, n = T*k; w read as [T*k]).  A src entry outside [0, n)
+ * gives 0 and is recorded (MOE_IDXERR_ROW).  The row scale of
+ * moe_grouped_gemm_bwd_scaled_gather and moe_act_bwd_scaled.
+ */
+moe_status moe_gather_scale(const float* w, const int32_t* src, int n, float* out,
+                            moe_stream_t stream);
+
+/*
+ * moe_grouped_gemm_bwd_scaled_gather -- GEMM 2's backward without the
+ * combine's gradient in memory [Brief, Core method: the grouped GEMM and
+ * its index generation; Summary, Method details / key design: optimised
+ * matrix multiplication].  The combine's backward would write
+ * dc[p, :] = row_scale[p] * dy[dc_rows[p] / dc_div, :] (row_scale: the gate
+ * weight of the slot held by row p, moe_gather_scale; dc_rows = src,
+ * dc_div = k); this call reads dy through the row map instead:
+ *   da[rows e] = diag(row_scale) (dy_g[rows e] @ b[e]^T)   [M, K] dtype
+ *   db[e]      = a_scaled[rows e]^T @ dy_g[rows e]          [E, K, N] float32
+ * with dy_g[p] = dy[dc_rows[p] / dc_div].  The scale of db sits on the
+ * activation operand: the caller passes a_scaled = diag(row_scale) a
+ * (moe_act_bwd_scaled writes it), which gives the same product
+ * a^T diag(row_scale) dy_g.  da is the float32 product times the scale,
+ * rounded once; db is float32 (zero for an empty group).
+ *   a_scaled [M, K], b [E, K, N], dy [dc_phys, N], da [M, K]: `dtype`
+ *   (bf16 only: the MFMA path, K and N multiples of 8, every pointer
+ *   16-byte aligned).  dc_rows int32 [M]; every dc_rows[p] / dc_div for the
+ *   rows the groups cover must lie in [0, dc_phys) (otherwise a zero row
+ *   stands in and MOE_IDXERR_GATHER is recorded).  row_scale float32 [M].
+ *   da or db may be NULL to skip that product.  Offsets, workspace and
+ *   errors as in moe_grouped_gemm_bwd.
+ */
+moe_status moe_grouped_gemm_bwd_scaled_gather(
+    const void* a_scaled, const void* b, const void* dy, const int32_t* dc_rows,
+    int dc_div, int dc_phys, const float* row_scale, const int32_t* offsets,
+    int M, int K, int N, int E, moe_dtype dtype, void* da, float* db, void* ws,
+    size_t ws_bytes, moe_stream_t stream);
+
+/*
  * moe_act_fwd -- SwiGLU activation [Summary, Method details / key design:
  * optimised activation]: a[m, f] = silu(h[m, f]) * h[m, F + f],
  * silu(z) = z / (1 + exp(-z)).   h [M, 2F], a [M, F], both `dtype`.
@@ -362,6 +405,17 @@ moe_status moe_act_fwd(const void* h, int M, int F, moe_dtype dtype, void* a,
                        moe_stream_t stream);
 moe_status moe_act_bwd(const void* h, const void* da, int M, int F,
                        moe_dtype dtype, void* dh, moe_stream_t stream);
+
+/*
+ * moe_act_bwd_scaled -- moe_act_bwd, plus the activation recomputed from h
+ * and scaled per row, for moe_grouped_gemm_bwd_scaled_gather:
+ * a_scaled[m, f] = row_scale[m] * silu(h[m, f]) * h[m, F + f], rounded once
+ * to dtype.  dh is bit for bit the result of moe_act_bwd.
+ *   h, dh [M, 2F], da, a_scaled [M, F]: `dtype`.  row_scale float32 [M].
+ */
+moe_status moe_act_bwd_scaled(const void* h, const void* da, const float* row_scale,
+                              int M, int F, moe_dtype dtype, void* dh, void* a_scaled,
+                              moe_stream_t stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

@@ -42,7 +42,8 @@ SYMBOLS = (
     "moe_grouped_gemm_plan",
     "moe_grouped_gemm_fwd", "moe_grouped_gemm_bwd", "moe_grouped_gemm_swiglu_fwd",
     "moe_grouped_gemm_swiglu_fwd_gather", "moe_grouped_gemm_bwd_gather",
-    "moe_act_fwd", "moe_act_bwd",
+    "moe_act_fwd", "moe_act_bwd", "moe_gather_scale", "moe_grouped_gemm_bwd_scaled_gather",
+    "moe_act_bwd_scaled",
 )
 
 
@@ -111,6 +112,10 @@ _SIG = {
                                      _p, _z, _p], _i),
     "moe_act_fwd": ([_p, _i, _i, _i, _p, _p], _i),
     "moe_act_bwd": ([_p, _p, _i, _i, _i, _p, _p], _i),
+    "moe_gather_scale": ([_p, _p, _i, _p, _p], _i),
+    "moe_grouped_gemm_bwd_scaled_gather": ([_p, _p, _p, _p, _i, _i, _p, _p, _i, _i, _i, _i, _i,
+                                            _p, _p, _p, _z, _p], _i),
+    "moe_act_bwd_scaled": ([_p, _p, _p, _i, _i, _i, _p, _p, _p], _i),
 }
 for _name, (_args, _res) in _SIG.items():
     _f = getattr(_lib, _name)
@@ -269,3 +274,21 @@ def moe_act_fwd(h, M, F, dtype, a, stream=None):
 
 def moe_act_bwd(h, da, M, F, dtype, dh, stream=None):
     _check(_lib.moe_act_bwd(_ptr(h), _ptr(da), M, F, dtype, _ptr(dh), _stream(stream, h)))
+
+
+def moe_gather_scale(w, src, n, out, stream=None):
+    _check(_lib.moe_gather_scale(_ptr(w), _ptr(src), n, _ptr(out), _stream(stream, out)))
+
+
+def moe_grouped_gemm_bwd_scaled_gather(a_scaled, b, dy, dc_rows, dc_div, dc_phys, row_scale,
+                                       offsets, M, K, N, E, dtype, da, db, ws=None, ws_bytes=0,
+                                       stream=None):
+    _check(_lib.moe_grouped_gemm_bwd_scaled_gather(
+        _ptr(a_scaled), _ptr(b), _ptr(dy), _ptr(dc_rows), dc_div, dc_phys, _ptr(row_scale),
+        _ptr(offsets), M, K, N, E, dtype, _ptr(da), _ptr(db), _ptr(ws), ws_bytes,
+        _stream(stream, dy)))
+
+
+def moe_act_bwd_scaled(h, da, row_scale, M, F, dtype, dh, a_scaled, stream=None):
+    _check(_lib.moe_act_bwd_scaled(_ptr(h), _ptr(da), _ptr(row_scale), M, F, dtype, _ptr(dh),
+                                   _ptr(a_scaled), _stream(stream, h)))

@@ -107,6 +107,39 @@ __global__ __launch_bounds__(kActBlock) void act_bwd_kernel(const T* __restrict_
   }
 }
 
+// act_bwd plus the activation itself, recomputed from h and scaled by a
+// per-row factor: a_s[m, :] = row_scale[m] * silu(G) * U, rounded once.  It
+// feeds GEMM 2's weight gradient when the combine's gradient is read through
+// the row map instead of being written (the gate weight moves from dc to a).
+template <typename T>
+__global__ __launch_bounds__(kActBlock) void act_bwd_scaled_kernel(
+    const T* __restrict__ h, const T* __restrict__ da, const float* __restrict__ row_scale, int M,
+    int F, T* __restrict__ dh, T* __restrict__ a_s) {
+  constexpr int N = Elems<T>::N;
+  const int cpr = F / N;
+  const int total = M * cpr;
+  for (int i = blockIdx.x * kActBlock + threadIdx.x; i < total; i += gridDim.x * kActBlock) {
+    const int m = i / cpr, c = i - m * cpr;
+    const T* hr = h + static_cast<size_t>(m) * 2 * F + c * N;
+    float g[N], u[N], d[N], dg[N], du[N], o[N];
+    load_f32<true>(hr, g);
+    load_f32<true>(hr + F, u);
+    load_f32<true>(da + static_cast<size_t>(m) * F + c * N, d);
+    const float rs = row_scale[m];
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      const float s = sigmoid_fast(g[e]);
+      dg[e] = d[e] * u[e] * s * (1.f + g[e] * (1.f - s));
+      du[e] = d[e] * g[e] * s;
+      o[e] = rs * (g[e] * s * u[e]);
+    }
+    T* dr = dh + static_cast<size_t>(m) * 2 * F + c * N;
+    store_f32(dr, dg);
+    store_f32(dr + F, du);
+    store_f32(a_s + static_cast<size_t>(m) * F + c * N, o);
+  }
+}
+
 int act_grid(int M, int F, moe_dtype dt) {
   // One chunk per thread, capped at 32 workgroups per compute unit.
   const long long chunks = static_cast<long long>(M) * F * static_cast<long long>(dtype_size(dt)) / 16;
@@ -159,4 +192,24 @@ extern "C" moe_status moe_act_bwd(const void* h, const void* da, int M, int F, m
                        as_stream(stream), static_cast<const float*>(h),
                        static_cast<const float*>(da), M, F, static_cast<float*>(dh));
   return check_launch("moe_act_bwd");
+}
+
+extern "C" moe_status moe_act_bwd_scaled(const void* h, const void* da, const float* row_scale,
+                                         int M, int F, moe_dtype dtype, void* dh, void* a_scaled,
+                                         moe_stream_t stream) {
+  clear_error();
+  if (moe_status s = check_act(M, F, dtype)) return s;
+  MOE_REQUIRE(h && da && row_scale && dh && a_scaled, MOE_ERR_INVALID_ARG,
+              "moe_act_bwd_scaled: null pointer");
+  const dim3 grid(act_grid(M, F, dtype)), block(kActBlock);
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(act_bwd_scaled_kernel<uint16_t>, grid, block, 0, as_stream(stream),
+                       static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(da),
+                       row_scale, M, F, static_cast<uint16_t*>(dh),
+                       static_cast<uint16_t*>(a_scaled));
+  else
+    hipLaunchKernelGGL(act_bwd_scaled_kernel<float>, grid, block, 0, as_stream(stream),
+                       static_cast<const float*>(h), static_cast<const float*>(da), row_scale, M,
+                       F, static_cast<float*>(dh), static_cast<float*>(a_scaled));
+  return check_launch("moe_act_bwd_scaled");
 }

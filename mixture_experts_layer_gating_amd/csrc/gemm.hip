@@ -73,6 +73,17 @@ struct GemmArgs {
   int xshift;       // log2(xdiv) when xdiv is a power of two, else -1
   int hot_first;    // TN, E <= 256: take the groups in hot-first order (group_at)
   int row_group;    // NN / NT: tile order inside a group (see find_row_tile); 0 = row-major
+  // Gathered y operand (the weight gradient reading its dc through a row
+  // map): logical row p of y is physical row yrows[p] / ydiv of an array of
+  // yphys rows.  yrows == nullptr: y is used as is.
+  const int32_t* yrows;
+  int ydiv;
+  int yphys;
+  unsigned ymagic;
+  int yshift;
+  // NT: output row p is multiplied by row_scale[p] before rounding (nullptr:
+  // no scale).
+  const float* row_scale;
 };
 
 // ------------------------------------------------------------------ tiles
@@ -797,6 +808,7 @@ __device__ __forceinline__ void reduce_tile(f32x16 (&acc)[MI][NI], XL& xl, YL& y
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     xl.prepare(s);
+    yl.prepare(s);
     issue_step<XS, YS>(xl, yl, xb, yb, s, s);
   }
   wait_vmcnt<3 * LQ + LP>();
@@ -811,7 +823,8 @@ __device__ __forceinline__ void reduce_tile(f32x16 (&acc)[MI][NI], XL& xl, YL& y
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const bool live = !decltype(guarded)::value || kt + s < nk;
-      xl.prepare(s);  // gathered x: rows of the call this step issues
+      xl.prepare(s);  // gathered operands: rows of the call this step issues
+      yl.prepare(s);
       read_frags<MIV, XS, YS>(f1, xb, yb, s, 1, xa, ya);
       if (live) mfma_step<MIV>(acc, f0);
       interleave_mfma_ds<MIV * NI>();
@@ -845,7 +858,7 @@ __device__ __forceinline__ void reduce_tile(f32x16 (&acc)[MI][NI], XL& xl, YL& y
 // GX: the x operand is gathered through p.xrows (GEMM 1 with the SwiGLU
 // epilogue, and the weight gradient).
 template <int MODE, int BM, int BN, int WGM, int WGN, typename OutT, bool GLU = false,
-          bool GX = false>
+          bool GX = false, bool GY = false>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p) {
   constexpr bool XS = (MODE == kTN);  // x operand k-strided in memory
   constexpr bool YS = (MODE != kNT);  // y operand k-strided in memory
@@ -854,7 +867,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
   constexpr int MI = WM / 32, NI = WN / 32;
   static_assert(!GLU || (MODE == kNN && NI == 2 && sizeof(OutT) == 2),
                 "the SwiGLU epilogue pairs a wave's two column blocks");
-  static_assert(!GX || GLU || MODE == kTN, "gathered x: GEMM 1 with SwiGLU, weight gradient");
+  static_assert(!GX || GLU || MODE == kTN || MODE == kNT,
+                "gathered x: GEMM 1 with SwiGLU, data and weight gradients");
+  static_assert(!GY || (MODE == kTN && !GX), "gathered y: weight gradient, x not gathered");
   // Elements per buffer: four quad buffers (k-strided) or two pair buffers.
   constexpr int XBE = XS ? BM * kBK : BM * 2 * kBK;
   constexpr int YBE = YS ? BN * kBK : BN * 2 * kBK;
@@ -898,10 +913,19 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
           t.g1 - t.i0, 0, 0};
     yo = {static_cast<const uint16_t*>(p.y) + t.e * KN + j0, p.N, p.N - j0, 0, 0};
   } else if constexpr (MODE == kNT) {
-    xo = {static_cast<const uint16_t*>(p.x) + static_cast<long long>(t.i0) * p.N, p.N,
-          t.g1 - t.i0, 0, 0};
+    if constexpr (GX)
+      xo = {static_cast<const uint16_t*>(p.x), p.N, t.g1 - t.i0, 0, 0, p.xrows + t.i0, p.xdiv,
+            p.xphys, 0, p.xmagic, p.xshift};
+    else
+      xo = {static_cast<const uint16_t*>(p.x) + static_cast<long long>(t.i0) * p.N, p.N,
+            t.g1 - t.i0, 0, 0};
     yo = {static_cast<const uint16_t*>(p.y) + t.e * KN + static_cast<long long>(j0) * p.N, p.N,
           p.K - j0, 0, 0};
+  } else if constexpr (GY) {
+    xo = {static_cast<const uint16_t*>(p.x) + static_cast<long long>(t.r_lo) * p.K + t.i0, p.K,
+          p.K - t.i0, 0, 0};
+    yo = {static_cast<const uint16_t*>(p.y), p.N, p.N - j0, 0, 0, p.yrows, p.ydiv, p.yphys, j0,
+          p.ymagic, p.yshift};
   } else if constexpr (GX) {
     xo = {static_cast<const uint16_t*>(p.x), p.K, p.K - t.i0, 0, 0, p.xrows, p.xdiv, p.xphys,
           t.i0, p.xmagic, p.xshift};
@@ -914,7 +938,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
           p.N - j0, 0, 0};
   }
   DmaLoader<XS, BM, NW, GX> xl;
-  DmaLoader<YS, BN, NW> yl;
+  DmaLoader<YS, BN, NW, GY> yl;
   xl.init(xo, t.r_lo, t.r_hi);
   yl.init(yo, t.r_lo, t.r_hi);
 
@@ -961,6 +985,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
   }
   if constexpr (GX) {
     if ((__ballot(xl.g_bad) | xl.g_badmask) != 0 && lane == 0) note_index_error(MOE_IDXERR_GATHER);
+  }
+  if constexpr (GY) {
+    if (yl.g_badmask != 0 && lane == 0) note_index_error(MOE_IDXERR_GATHER);
   }
 
   if constexpr (GLU) {
@@ -1044,10 +1071,28 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
                        ? static_cast<unsigned>(((wm * WM + (lane >> 5) * 4) * ld + col) * SZ)
                        : kOOB;
     }
+    // Gathered NT (the data gradient of GEMM 2 reading dy through the row
+    // map): output row p is scaled by row_scale[p] (the slot's gate weight)
+    // before rounding; the scales of this lane's rows of block i are loaded
+    // once for all its column blocks.
+    constexpr bool kScaled = MODE == kNT && GX;
+    const __amdgpu_buffer_rsrc_t sc_rs =
+        make_rsrc(kScaled ? static_cast<const void*>(p.row_scale + t.i0) : p.out,
+                  kScaled ? static_cast<long long>(rows) * 4 : 0);
+    const unsigned sc_lane = static_cast<unsigned>((wm * WM + (lane >> 5) * 4) * 4);
     // The stores, with the (NT) addend read from the same offsets.
     auto store_all = [&](auto with_add) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
+        float sc[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sc[r] = 1.f;
+          if constexpr (kScaled)
+            sc[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                sc_rs, sc_lane + static_cast<unsigned>((i * 32 + (r >> 2) * 8 + (r & 3)) * 4), 0,
+                0));
+        }
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
           // A block's addend values are all read before any of its stores
@@ -1067,6 +1112,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_mfma_kernel(GemmArgs p
             const int row_c = i * 32 + (r >> 2) * 8 + (r & 3);
             const unsigned off = col_off[j] + static_cast<unsigned>(row_c * ld * SZ);
             float v = acc[i][j][r];
+            if constexpr (kScaled) v *= sc[r];
             if constexpr (decltype(with_add)::value) v += addv[r];
             if constexpr (SZ == 2)
               __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), out_rs, off, 0, 0);
@@ -1287,14 +1333,14 @@ bool mfma_ok(moe_dtype dt, int M, int K, int N) {
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; }
 
 template <int MODE, int BM, int BN, int WGM, int WGN, typename OutT, bool GLU = false,
-          bool GX = false>
+          bool GX = false, bool GY = false>
 void launch_mfma(GemmArgs p, long long tiles_upper, hipStream_t st) {
   const long long grid = ceil_div(tiles_upper, 8) * 8;
-  hipLaunchKernelGGL((gemm_mfma_kernel<MODE, BM, BN, WGM, WGN, OutT, GLU, GX>),
+  hipLaunchKernelGGL((gemm_mfma_kernel<MODE, BM, BN, WGM, WGN, OutT, GLU, GX, GY>),
                      dim3(static_cast<unsigned>(grid)), dim3(64 * WGM * WGN), 0, st, p);
 }
 
-template <int MODE, typename OutT, bool GX = false>
+template <int MODE, typename OutT, bool GX = false, bool GY = false>
 void dispatch_mfma(Cfg c, GemmArgs p, hipStream_t st) {
   const int ncols = (MODE == kNN) ? p.N : (MODE == kNT ? p.K : p.N);
   p.ntn = static_cast<int>(ceil_div(ncols, c.bn));
@@ -1308,10 +1354,14 @@ void dispatch_mfma(Cfg c, GemmArgs p, hipStream_t st) {
   } else {
     upper = (ceil_div(p.M, c.bm) + p.E) * p.ntn;
   }
-  if (c.bm == 256 && c.bn == 256) launch_mfma<MODE, 256, 256, 2, 4, OutT, false, GX>(p, upper, st);
-  else if (c.bm == 128 && c.bn == 128) launch_mfma<MODE, 128, 128, 2, 2, OutT, false, GX>(p, upper, st);
-  else if (c.bm == 64 && c.bn == 256) launch_mfma<MODE, 64, 256, 1, 4, OutT, false, GX>(p, upper, st);
-  else launch_mfma<MODE, 64, 64, 2, 2, OutT, false, GX>(p, upper, st);
+  if (c.bm == 256 && c.bn == 256)
+    launch_mfma<MODE, 256, 256, 2, 4, OutT, false, GX, GY>(p, upper, st);
+  else if (c.bm == 128 && c.bn == 128)
+    launch_mfma<MODE, 128, 128, 2, 2, OutT, false, GX, GY>(p, upper, st);
+  else if (c.bm == 64 && c.bn == 256)
+    launch_mfma<MODE, 64, 256, 1, 4, OutT, false, GX, GY>(p, upper, st);
+  else
+    launch_mfma<MODE, 64, 64, 2, 2, OutT, false, GX, GY>(p, upper, st);
 }
 
 // GEMM 1 with the SwiGLU epilogue: tiles of 128 hidden units (gate and up
@@ -1625,4 +1675,72 @@ extern "C" moe_status moe_grouped_gemm_bwd_gather(const void* a, const int32_t* 
               "moe_grouped_gemm_bwd_gather: needs the bf16 MFMA path (K, N multiples of 8)");
   return grouped_gemm_bwd(a, a_rows, a_div, a_phys, b, dc, offsets, M, K, N, E, dtype, da, da_add,
                           db, ws, ws_bytes, stream);
+}
+
+extern "C" moe_status moe_grouped_gemm_bwd_scaled_gather(
+    const void* a_scaled, const void* b, const void* dy, const int32_t* dc_rows, int dc_div,
+    int dc_phys, const float* row_scale, const int32_t* offsets, int M, int K, int N, int E,
+    moe_dtype dtype, void* da, float* db, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  clear_error();
+  if (moe_status s = check_gemm(offsets, M, K, N, E, dtype)) return s;
+  MOE_REQUIRE(dy != nullptr && row_scale != nullptr, MOE_ERR_INVALID_ARG,
+              "moe_grouped_gemm_bwd_scaled_gather: null dy or row_scale");
+  MOE_REQUIRE(da == nullptr || b != nullptr, MOE_ERR_INVALID_ARG,
+              "moe_grouped_gemm_bwd_scaled_gather: da needs b");
+  MOE_REQUIRE(db == nullptr || a_scaled != nullptr, MOE_ERR_INVALID_ARG,
+              "moe_grouped_gemm_bwd_scaled_gather: db needs a_scaled");
+  if (moe_status s = check_gather("moe_grouped_gemm_bwd_scaled_gather", dc_rows, dc_div, dc_phys, N))
+    return s;
+  MOE_REQUIRE(mfma_ok(dtype, M, K, N), MOE_ERR_UNSUPPORTED,
+              "moe_grouped_gemm_bwd_scaled_gather: needs the bf16 MFMA path (K, N multiples of 8)");
+  MOE_REQUIRE(aligned16(a_scaled) && aligned16(b) && aligned16(dy) && aligned16(da) &&
+                  aligned16(db),
+              MOE_ERR_INVALID_ARG,
+              "moe_grouped_gemm_bwd_scaled_gather: operands and results must be 16-byte aligned");
+  int split = 1;
+  if (db) {
+    split = pick_split(M, K, N, E);
+    if (split > 1) {
+      const size_t need = moe_grouped_gemm_workspace_size(M, K, N, E, dtype);
+      MOE_REQUIRE(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE,
+                  "moe_grouped_gemm_bwd_scaled_gather: workspace too small");
+      MOE_REQUIRE((reinterpret_cast<uintptr_t>(ws) & 15) == 0, MOE_ERR_WORKSPACE,
+                  "moe_grouped_gemm_bwd_scaled_gather: workspace must be 16-byte aligned");
+    }
+  }
+  hipStream_t st = as_stream(stream);
+  const unsigned magic = div_magic(dc_div);
+  const int shift = div_shift(dc_div);
+  if (da) {
+    // da = diag(row_scale) (dy_g @ b^T): the NT kernel with its x operand
+    // gathered and the scale in the epilogue.
+    GemmArgs p{dy, b, nullptr, da, offsets, M, K, N, E, 0, 0, 1, nullptr, dc_rows, dc_div,
+               dc_phys, magic, shift};
+    p.row_scale = row_scale;
+    dispatch_mfma<kNT, uint16_t, true>(pick_row_cfg(M, E, K), p, st);
+    if (moe_status s = check_launch("moe_grouped_gemm_bwd_scaled_gather/da")) return s;
+  }
+  if (db) {
+    // db = a_scaled^T @ dy_g: the TN kernel with its y operand gathered.
+    const int hot_first = split == 1 && E >= 2 && E <= 256 && M / E >= 128 ? 1 : 0;
+    GemmArgs p{a_scaled, dy, nullptr, split > 1 ? ws : static_cast<void*>(db), offsets, M, K,
+               N, E, 0, 0, split};
+    p.hot_first = hot_first;
+    p.yrows = dc_rows;
+    p.ydiv = dc_div;
+    p.yphys = dc_phys;
+    p.ymagic = magic;
+    p.yshift = shift;
+    dispatch_mfma<kTN, float, false, true>(pick_tn_cfg(K, N, E), p, st);
+    if (moe_status s = check_launch("moe_grouped_gemm_bwd_scaled_gather/db")) return s;
+    if (split > 1) {
+      const long long n = static_cast<long long>(E) * K * N;
+      long long g = ceil_div(n, 256);
+      if (g > 8192) g = 8192;
+      hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<unsigned>(g)), dim3(256), 0, st,
+                         static_cast<const float*>(ws), n, split, db);
+      if (moe_status s = check_launch("moe_grouped_gemm_bwd_scaled_gather/db")) return s;
+    }
+  }
+  return MOE_OK;
 }

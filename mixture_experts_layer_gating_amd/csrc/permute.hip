@@ -155,8 +155,9 @@ __global__ __launch_bounds__(kMoveBlock) void unpermute_kernel(const char* __res
   if (bad) note_index_error(MOE_IDXERR_ROW);
 }
 
-// One block per token: dyp rows of its k slots and the k dot products dw.
-template <typename T>
+// One block per token: dyp rows of its k slots (unless !WRITE_DYP) and the
+// k dot products dw.
+template <typename T, bool WRITE_DYP>
 __global__ __launch_bounds__(kMoveBlock) void unpermute_bwd_kernel(
     const char* __restrict__ dy, const char* __restrict__ yp, const int32_t* __restrict__ dest,
     const float* __restrict__ w, int k, unsigned rows, int chunks_per_row,
@@ -206,7 +207,8 @@ __global__ __launch_bounds__(kMoveBlock) void unpermute_bwd_kernel(
             dot[j0 + u] = fmaf(g[q], v[q], dot[j0 + u]);
             o[q] = wt * g[q];
           }
-          if (ok[u]) st16(dyp + static_cast<size_t>(dd[u]) * row_bytes + c * 16, Chunk<T>::pack(o));
+          if (WRITE_DYP && ok[u])
+            st16(dyp + static_cast<size_t>(dd[u]) * row_bytes + c * 16, Chunk<T>::pack(o));
         }
       }
     }
@@ -226,6 +228,21 @@ __global__ __launch_bounds__(kMoveBlock) void unpermute_bwd_kernel(
     for (int q = 0; q < kMoveBlock / kWave; ++q) acc += part[q][threadIdx.x];
     dw[static_cast<size_t>(t) * k + threadIdx.x] = acc;
   }
+}
+
+// out[p] = w[src[p]]: the gate weights in the expert-sorted row order (one
+// float per row; an entry of src outside [0, n) gives 0 and is recorded).
+__global__ __launch_bounds__(kMoveBlock) void gather_scale_kernel(const float* __restrict__ w,
+                                                                  const int32_t* __restrict__ src,
+                                                                  int n, float* __restrict__ out) {
+  bool bad = false;
+  for (int p = blockIdx.x * kMoveBlock + threadIdx.x; p < n; p += gridDim.x * kMoveBlock) {
+    const int s = src[p];
+    const bool ok = row_ok(s, static_cast<unsigned>(n));
+    bad |= !ok;
+    out[p] = ok ? w[s] : 0.f;
+  }
+  if (bad) note_index_error(MOE_IDXERR_ROW);
 }
 
 int row_grid(long long rows) {
@@ -287,19 +304,35 @@ extern "C" moe_status moe_unpermute_bwd(const void* dy, const void* yp, const in
                                         void* dyp, float* dw, moe_stream_t stream) {
   clear_error();
   if (moe_status s = check_move(T, k, d, dtype)) return s;
-  MOE_REQUIRE(dy && yp && dest && w && dyp && dw, MOE_ERR_INVALID_ARG,
+  MOE_REQUIRE(dy && yp && dest && w && dw, MOE_ERR_INVALID_ARG,
               "moe_unpermute_bwd: null pointer");
   const int cpr = static_cast<int>(d * dtype_size(dtype) / 16);
   const unsigned rows = static_cast<unsigned>(T) * static_cast<unsigned>(k);
-  if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(unpermute_bwd_kernel<uint16_t>, dim3(T), dim3(kMoveBlock), 0,
-                       as_stream(stream), static_cast<const char*>(dy),
-                       static_cast<const char*>(yp), dest, w, k, rows, cpr,
-                       static_cast<char*>(dyp), dw);
-  else
-    hipLaunchKernelGGL(unpermute_bwd_kernel<float>, dim3(T), dim3(kMoveBlock), 0,
-                       as_stream(stream), static_cast<const char*>(dy),
-                       static_cast<const char*>(yp), dest, w, k, rows, cpr,
-                       static_cast<char*>(dyp), dw);
+  const dim3 grid(T), block(kMoveBlock);
+  hipStream_t st = as_stream(stream);
+  const char* dyc = static_cast<const char*>(dy);
+  const char* ypc = static_cast<const char*>(yp);
+  char* dypc = static_cast<char*>(dyp);
+#define MOE_UBWD(TT, WD)                                                                       \
+  hipLaunchKernelGGL((unpermute_bwd_kernel<TT, WD>), grid, block, 0, st, dyc, ypc, dest, w, k, \
+                     rows, cpr, dypc, dw)
+  if (dtype == MOE_BF16) {
+    if (dyp) MOE_UBWD(uint16_t, true); else MOE_UBWD(uint16_t, false);
+  } else {
+    if (dyp) MOE_UBWD(float, true); else MOE_UBWD(float, false);
+  }
+#undef MOE_UBWD
   return check_launch("moe_unpermute_bwd");
+}
+
+extern "C" moe_status moe_gather_scale(const float* w, const int32_t* src, int n, float* out,
+                                       moe_stream_t stream) {
+  clear_error();
+  MOE_REQUIRE(n >= 1, MOE_ERR_INVALID_ARG, "moe_gather_scale: n must be >= 1");
+  MOE_REQUIRE(w && src && out, MOE_ERR_INVALID_ARG, "moe_gather_scale: null pointer");
+  long long g = (static_cast<long long>(n) + kMoveBlock - 1) / kMoveBlock;
+  if (g > 2048) g = 2048;
+  hipLaunchKernelGGL(gather_scale_kernel, dim3(static_cast<unsigned>(g)), dim3(kMoveBlock), 0,
+                     as_stream(stream), w, src, n, out);
+  return check_launch("moe_gather_scale");
 }

@@ -27,6 +27,13 @@ Backward of <y, dy> (the forward-plus-backward unit of [Brief, Key results]):
     dxp       moe_grouped_gemm_bwd        dx_e      moe_unpermute (w = NULL)
     dW1       moe_grouped_gemm_bwd        dlogits   moe_route_topk_bwd
     dx = dx_e + dlogits @ wr^T, dwr = x^T @ dlogits   moe_grouped_gemm_bwd
+
+With ``gather_dy`` (the default where the bf16 MFMA path applies) the
+combine's gradient dyp = w * dy[src // k] is never written: the combine's
+backward computes dw only, and GEMM 2's backward reads dy through the row map
+with the gate weight as a row scale (moe_gather_scale,
+moe_grouped_gemm_bwd_scaled_gather; its weight gradient takes the scale on
+the activation, written by moe_act_bwd_scaled).
 """
 from __future__ import annotations
 
@@ -69,7 +76,8 @@ class MoELayer:
     RECOMPUTE = ("none", "act", "layer")
 
     def __init__(self, T, d, E, k, F, dtype=torch.bfloat16, device="cuda", renorm=False,
-                 fuse_act=True, overlap_wgrad=False, gather_x=True, recompute="none"):
+                 fuse_act=True, overlap_wgrad=False, gather_x=True, recompute="none",
+                 gather_dy=True):
         if not (1 <= k <= E):
             raise ValueError("need 1 <= k <= E")
         if recompute not in self.RECOMPUTE:
@@ -85,6 +93,10 @@ class MoELayer:
         # instead of a permuted copy (bf16, fused activation, MFMA shapes).
         plan = L.moe_grouped_gemm_plan(3, T * k, d, 2 * F, E, self.code)
         self.gather_x = bool(gather_x) and self.fuse_act and bool(plan["mfma"])
+        # GEMM 2's backward reads dy through src / k, scaled by the gate
+        # weight, instead of a written dyp (bf16 MFMA shapes).
+        plan2 = L.moe_grouped_gemm_plan(1, T * k, F, d, E, self.code)
+        self.gather_dy = bool(gather_dy) and bool(plan2["mfma"])
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
@@ -112,7 +124,12 @@ class MoELayer:
         self.yp = torch.empty(Tk, d, dtype=dtype, device=dev)
         self.y = torch.empty(T, d, dtype=dtype, device=dev)
         # backward
-        self.dyp = torch.empty(Tk, d, dtype=dtype, device=dev)
+        if self.gather_dy:
+            self.dyp = None
+            self.w_sorted = torch.empty(Tk, dtype=f32, device=dev)
+            self.a_scaled = torch.empty(Tk, F, dtype=dtype, device=dev)
+        else:
+            self.dyp = torch.empty(Tk, d, dtype=dtype, device=dev)
         self.dw = torch.empty(T, k, dtype=f32, device=dev)
         self.da = torch.empty(Tk, F, dtype=dtype, device=dev)
         self.dh = torch.empty(Tk, 2 * F, dtype=dtype, device=dev)
@@ -218,7 +235,10 @@ class MoELayer:
             return {}
         kept = {n: getattr(self, n) for n in ("probs", "idx", "w", "offsets", "dest", "src",
                                                "h", "a", "yp")}
-        if mode == "act":
+        if mode == "act" or self.gather_dy:
+            # the backward reads `a` only for GEMM 2's weight gradient, and not
+            # at all when that gradient takes the scaled activation written by
+            # the SwiGLU backward
             del kept["a"]
         return {n: t.numel() * t.element_size() for n, t in kept.items()}
 
@@ -262,6 +282,66 @@ class MoELayer:
             L.moe_grouped_gemm_bwd(self.xp, w1, self.dh, self.offsets, Tk, d, 2 * F, E, c, None,
                                    None, self.dw1, ws, wsb, stream=stream)
 
+    def _gemm2_bwd(self, w2, ws, wsb, main, overlap):
+        """GEMM 2's backward from the written dyp; the SwiGLU backward."""
+        T, d, E, k, F, Tk, c = self.T, self.d, self.E, self.k, self.F, self.Tk, self.code
+        if self.recompute == "act":
+            # a was not kept: recompute it from the stored h (the same
+            # arithmetic as GEMM 1's activation epilogue, so the same bits)
+            # for GEMM 2's weight gradient.
+            with self._span("act_fwd_recompute"):
+                L.moe_act_fwd(self.h, Tk, F, c, self.a, stream=main)
+        if overlap:
+            self.ev_dyp.record(main)
+        with self._span("gemm2_bwd_da"):
+            # data gradient only: the activation operand `a` is not read
+            L.moe_grouped_gemm_bwd(None, w2, self.dyp, self.offsets, Tk, F, d, E, c, self.da,
+                                   None, None, ws, wsb, stream=main)
+        with self._span("act_bwd"):
+            L.moe_act_bwd(self.h, self.da, Tk, F, c, self.dh, stream=main)
+        if overlap:
+            self.ev_dh.record(main)
+            side, ws2 = self.side, self.gemm_ws2
+            side.wait_event(self.ev_dyp)
+            with torch.cuda.stream(side):
+                with self._span("gemm2_bwd_dw"):
+                    L.moe_grouped_gemm_bwd(self.a, w2, self.dyp, self.offsets, Tk, F, d, E, c,
+                                           None, None, self.dw2, ws2, wsb, stream=side)
+        else:
+            with self._span("gemm2_bwd_dw"):
+                L.moe_grouped_gemm_bwd(self.a, w2, self.dyp, self.offsets, Tk, F, d, E, c, None,
+                                       None, self.dw2, ws, wsb, stream=main)
+
+    def _gemm2_bwd_gathered(self, dy, w2, ws, wsb, main, overlap):
+        """GEMM 2's backward reading dy through src / k with the gate weight
+        as a row scale (dyp is never written); the SwiGLU backward, which
+        also writes the scaled activation for the weight gradient (so `a`
+        itself is not read in the backward pass, whatever ``recompute``)."""
+        T, d, E, k, F, Tk, c = self.T, self.d, self.E, self.k, self.F, self.Tk, self.code
+        with self._span("gather_scale"):
+            L.moe_gather_scale(self.w, self.src, Tk, self.w_sorted, stream=main)
+        with self._span("gemm2_bwd_da"):
+            L.moe_grouped_gemm_bwd_scaled_gather(None, w2, dy, self.src, k, T, self.w_sorted,
+                                                 self.offsets, Tk, F, d, E, c, self.da, None,
+                                                 stream=main)
+        with self._span("act_bwd"):
+            L.moe_act_bwd_scaled(self.h, self.da, self.w_sorted, Tk, F, c, self.dh,
+                                 self.a_scaled, stream=main)
+        if overlap:
+            self.ev_dh.record(main)
+            side, ws2 = self.side, self.gemm_ws2
+            side.wait_event(self.ev_dh)
+            with torch.cuda.stream(side):
+                with self._span("gemm2_bwd_dw"):
+                    L.moe_grouped_gemm_bwd_scaled_gather(
+                        self.a_scaled, None, dy, self.src, k, T, self.w_sorted, self.offsets, Tk,
+                        F, d, E, c, None, self.dw2, ws2, wsb, stream=side)
+        else:
+            with self._span("gemm2_bwd_dw"):
+                L.moe_grouped_gemm_bwd_scaled_gather(
+                    self.a_scaled, None, dy, self.src, k, T, self.w_sorted, self.offsets, Tk, F,
+                    d, E, c, None, self.dw2, ws, wsb, stream=main)
+
     def backward(self, dy, stream=None):
         if self._inputs is None:
             raise RuntimeError("backward() before forward()")
@@ -281,39 +361,20 @@ class MoELayer:
         with self._span("unpermute_bwd"):
             L.moe_unpermute_bwd(dy, self.yp, self.dest, self.w, T, k, d, c, self.dyp, self.dw,
                                 stream=main)
-        if self.recompute == "act":
-            # a was not kept: recompute it from the stored h (the same
-            # arithmetic as GEMM 1's activation epilogue, so the same bits)
-            # for GEMM 2's weight gradient.
-            with self._span("act_fwd_recompute"):
-                L.moe_act_fwd(self.h, Tk, F, c, self.a, stream=main)
+        if self.gather_dy:
+            self._gemm2_bwd_gathered(dy, w2, ws, wsb, main, overlap)
+        else:
+            self._gemm2_bwd(w2, ws, wsb, main, overlap)
         if overlap:
-            self.ev_dyp.record(main)
-        with self._span("gemm2_bwd_da"):
-            # data gradient only: the activation operand `a` is not read
-            L.moe_grouped_gemm_bwd(None, w2, self.dyp, self.offsets, Tk, F, d, E, c, self.da,
-                                   None, None, ws, wsb, stream=main)
-        with self._span("act_bwd"):
-            L.moe_act_bwd(self.h, self.da, Tk, F, c, self.dh, stream=main)
-        if overlap:
-            # Weight gradients on the side stream: dW2 once dyp exists, dW1
-            # once dh exists; they fill the compute units the data-gradient
-            # chain leaves idle (kernel tails, memory-bound kernels).
-            self.ev_dh.record(main)
-            side, ws2 = self.side, self.gemm_ws2
-            side.wait_event(self.ev_dyp)
+            # dW1 follows dW2 on the side stream once dh exists; both fill the
+            # compute units the data-gradient chain leaves idle (kernel tails,
+            # memory-bound kernels).
+            side = self.side
             with torch.cuda.stream(side):
-                with self._span("gemm2_bwd_dw"):
-                    L.moe_grouped_gemm_bwd(self.a, w2, self.dyp, self.offsets, Tk, F, d, E, c,
-                                           None, None, self.dw2, ws2, wsb, stream=side)
                 side.wait_event(self.ev_dh)
                 with self._span("gemm1_bwd_dw"):
-                    self._dw1(x, w1, ws2, wsb, side)
+                    self._dw1(x, w1, self.gemm_ws2, wsb, side)
             self.ev_side.record(side)
-        else:
-            with self._span("gemm2_bwd_dw"):
-                L.moe_grouped_gemm_bwd(self.a, w2, self.dyp, self.offsets, Tk, F, d, E, c, None,
-                                       None, self.dw2, ws, wsb, stream=main)
         with self._span("gemm1_bwd_da"):
             # data gradient only: the activation operand `a` is not read
             L.moe_grouped_gemm_bwd(None, w1, self.dh, self.offsets, Tk, d, 2 * F, E, c,

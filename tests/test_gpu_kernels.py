@@ -306,3 +306,88 @@ def test_grouped_gemm_gathered_x(T, k, d, F, E, pattern):
     # and against the oracle
     _, ref_db = O.grouped_matmul_backward(xp, w1, dh, off)
     assert rel(host(db1), ref_db) <= TOL_F32
+
+
+# ------------------------------------------------------------------ GEMM 2 backward, dy gathered
+def test_gather_scale():
+    say("gather_scale")
+    n = 5000
+    w = np.random.default_rng(21).random(n).astype(np.float32)
+    src = np.random.default_rng(22).permutation(n).astype(np.int32)
+    out = torch.empty(n, dtype=torch.float32, device=DEV)
+    L.moe_gather_scale(dev(w), dev(src), n, out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(out), w[src])
+
+
+@pytest.mark.parametrize("M,F", [(1, 8), (513, 264), (4096, 1024)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_swiglu_bwd_scaled(M, F, dtype):
+    """dh as moe_act_bwd bit for bit; the scaled activation s * silu(g) * u
+    against the oracle (one rounding), and with s = 1 bit for bit the
+    activation moe_act_fwd writes."""
+    say(f"swiglu bwd scaled M={M} F={F} {dtype}")
+    tdt = DTYPES[dtype]
+    code = L.dtype_code(tdt)
+    h = _normal((M, 2 * F), 31, dtype=dtype)
+    da = _normal((M, F), 32, dtype=dtype)
+    s = np.random.default_rng(33).random(M).astype(np.float32)
+    hd, dad = dev(h, tdt), dev(da, tdt)
+    dh0 = torch.empty(M, 2 * F, dtype=tdt, device=DEV)
+    L.moe_act_bwd(hd, dad, M, F, code, dh0)
+    dh1, as1 = torch.empty_like(dh0), torch.empty(M, F, dtype=tdt, device=DEV)
+    L.moe_act_bwd_scaled(hd, dad, dev(s), M, F, code, dh1, as1)
+    ones = torch.ones(M, dtype=torch.float32, device=DEV)
+    dh2, as2 = torch.empty_like(dh0), torch.empty_like(as1)
+    L.moe_act_bwd_scaled(hd, dad, ones, M, F, code, dh2, as2)
+    a0 = torch.empty_like(as1)
+    L.moe_act_fwd(hd, M, F, code, a0)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(dh1) if dtype == "bf16" else host(dh1),
+                                  bits(dh0) if dtype == "bf16" else host(dh0))
+    np.testing.assert_array_equal(bits(as2) if dtype == "bf16" else host(as2),
+                                  bits(a0) if dtype == "bf16" else host(a0))
+    ref = O.swiglu(h) * s[:, None]
+    assert rel(host(as1), ref) <= (TOL_ONE_ROUNDING if dtype == "bf16" else TOL_F32)
+
+
+SCALED_CASES = [(1024, 8, 256, 128, 16, "random"),   # 64x256 data-gradient tiles, 128x128 dW
+                (700, 3, 264, 136, 5, "empty"),      # ragged widths, an empty group
+                (4096, 2, 512, 256, 8, "skew"),      # 256x256 tiles
+                (333, 5, 128, 64, 7, "one"),         # every row in the last group
+                (2048, 1, 512, 64, 1, "uniform")]    # one group, 64-wide output
+
+
+@pytest.mark.parametrize("T,k,d,F,E,pattern", SCALED_CASES)
+def test_grouped_gemm_bwd_scaled_gather(T, k, d, F, E, pattern):
+    """GEMM 2's backward reading dy through src / k with a row scale: da
+    against the oracle on dc = diag(s) dy[src // k]; db bit for bit the plain
+    weight gradient on the gathered copy dy[src // k] with the scaled
+    activation, and against the oracle."""
+    say(f"grouped_gemm bwd scaled gather T={T} k={k} d={d} F={F} E={E} {pattern}")
+    bf, code = torch.bfloat16, L.MOE_BF16
+    M = T * k
+    off = _groups(M, E, pattern, 23)
+    src = np.random.default_rng(24).permutation(M).astype(np.int32)
+    dy = _normal((T, d), 25)
+    w2 = _normal((E, F, d), 26, scale=0.05)
+    a_s = _normal((M, F), 27)
+    s = np.random.default_rng(28).random(M).astype(np.float32)
+    dyg = dy[src // k]
+    dyd, srcd, w2d, offd, asd = dev(dy, bf), dev(src), dev(w2, bf), dev(off), dev(a_s, bf)
+    nb = L.moe_grouped_gemm_workspace_size(M, F, d, E, code)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=DEV)
+    da = torch.zeros(M, F, dtype=bf, device=DEV)
+    db1 = torch.full((E, F, d), -7.0, dtype=torch.float32, device=DEV)
+    L.moe_grouped_gemm_bwd_scaled_gather(asd, w2d, dyd, srcd, k, T, dev(s), offd, M, F, d, E, code,
+                                         da, db1, ws, nb)
+    db0 = torch.full_like(db1, 7.0)
+    L.moe_grouped_gemm_bwd(asd, w2d, dev(dyg, bf), offd, M, F, d, E, code, None, None, db0, ws,
+                           nb)
+    torch.cuda.synchronize()
+    rows = slice(0, int(off[-1]))
+    ref_da, _ = O.grouped_matmul_backward(a_s, w2, s[:, None].astype(np.float64) * dyg, off)
+    assert rel(host(da)[rows], ref_da[rows]) <= TOL_ONE_ROUNDING
+    np.testing.assert_array_equal(host(db1), host(db0))
+    _, ref_db = O.grouped_matmul_backward(a_s, w2, dyg, off)
+    assert rel(host(db1), ref_db) <= TOL_F32

@@ -24,12 +24,12 @@ def _native_lib():
     import mixture_experts_layer_gating_amd._lib  # noqa: F401  (raises if not built)
 
 
-def _run(inp, renorm=False, fuse_act=True, overlap_wgrad=False):
+def _run(inp, renorm=False, fuse_act=True, overlap_wgrad=False, gather_dy=True):
     from mixture_experts_layer_gating_amd.layer import MoELayer
     wl = inp.wl
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, dtype=tdt, device=DEV, renorm=renorm,
-                     fuse_act=fuse_act, overlap_wgrad=overlap_wgrad)
+                     fuse_act=fuse_act, overlap_wgrad=overlap_wgrad, gather_dy=gather_dy)
     x, wr, w1, w2, dy = (dev(a, tdt) for a in (inp.x, inp.wr, inp.w1, inp.w2, inp.dy))
     bias = None if inp.bias is None else dev(inp.bias)
     forced = None if inp.forced_idx is None else dev(inp.forced_idx)
@@ -39,10 +39,10 @@ def _run(inp, renorm=False, fuse_act=True, overlap_wgrad=False):
     return layer, grads, (x, wr, w1, w2, dy, bias, forced)
 
 
-def _full_compare(inp, renorm=False):
+def _full_compare(inp, renorm=False, gather_dy=True):
     wl = inp.wl
     tol = TOL_BF16 if wl.dtype == "bf16" else TOL_F32
-    layer, g, _ = _run(inp, renorm)
+    layer, g, _ = _run(inp, renorm, gather_dy=gather_dy)
     logits = host(layer.logits).astype(np.float32)
     # the device's logits agree with the oracle's own float64 logits (float32
     # sums of exactly representable products)
@@ -90,6 +90,15 @@ def test_layer_small_bf16(shape):
     wl = Workload("small", dtype="bf16", w_std=0.05, seed=sum(shape.values()), **shape)
     say(f"layer {wl}")
     _full_compare(make_inputs(wl))
+
+
+@pytest.mark.parametrize("shape", [SMALL[0], SMALL[1], SMALL[3]])
+def test_layer_written_dyp_bf16(shape):
+    """The backward pass with the combine's gradient written (gather_dy=False)
+    against the oracle, as the default gathered path is."""
+    wl = Workload("dyp", dtype="bf16", w_std=0.05, seed=sum(shape.values()) + 1, **shape)
+    say(f"layer written dyp {wl}")
+    _full_compare(make_inputs(wl), gather_dy=False)
 
 
 def test_layer_ragged_fp32():
@@ -282,7 +291,9 @@ def test_layer_recompute_modes_match(mode):
             np.testing.assert_array_equal(host(lb.y), want["y"])
     kept = lb.saved_bytes()
     full = lb.saved_bytes("none")
-    assert (kept == {}) if mode == "layer" else (set(full) - set(kept) == {"a"})
+    # with dy read through the row map (the default) the backward never reads
+    # `a`, so "none" already leaves it out
+    assert (kept == {}) if mode == "layer" else (kept == full and "a" not in kept)
 
 
 def test_layer_overlapped_weight_gradients_match():
