@@ -261,10 +261,10 @@ moe_status moe_unpermute_bwd(const void* dy, const void* yp,
  *   da or db may be NULL to skip that product; da_add may be NULL.
  *
  * The bf16 path runs on MFMA tiles when K % 8 == 0 and N % 8 == 0; other
- * shapes and float32 run on an LDS-tiled 64x64 kernel on the float32 matrix cores.  On the MFMA path every
- * operand and result pointer must be 16-byte aligned (MOE_ERR_INVALID_ARG
- * otherwise).  ws/ws_bytes: device workspace of at least
- * moe_grouped_gemm_workspace_size() bytes, 16-byte aligned, used by
+ * shapes and float32 run on an LDS-tiled 64x64 kernel on the float32 matrix
+ * cores.  On the MFMA path every operand and result pointer must be 16-byte
+ * aligned (MOE_ERR_INVALID_ARG otherwise).  ws/ws_bytes: device workspace
+ * of at least moe_grouped_gemm_workspace_size() bytes, 16-byte aligned, used by
  * moe_grouped_gemm_bwd for db when the weight gradient is reduced in row
  * slices (shapes with few output tiles); MOE_ERR_WORKSPACE if it is needed
  * and missing or too small.  The size is 0 (NULL allowed) when no slicing is
@@ -276,10 +276,11 @@ size_t moe_grouped_gemm_workspace_size(int M, int K, int N, int E,
  * moe_grouped_gemm_plan -- the kernel configuration the grouped GEMM entry
  * points choose for a shape (host-only query, enqueues nothing).
  * product: 0 = forward c (moe_grouped_gemm_fwd), 1 = da, 2 = db
- * (moe_grouped_gemm_bwd), 3 = h of moe_grouped_gemm_swiglu_fwd (N = 2F).  Writes the row/column tile sizes, the wavefront
- * grid of a workgroup (waves_m x waves_n), and the number of reduction
- * slices; *mfma = 1 for the bf16 MFMA kernel, 0 for the float32-MFMA kernel.  Any
- * output pointer may be NULL.
+ * (moe_grouped_gemm_bwd), 3 = h of moe_grouped_gemm_swiglu_fwd (N = 2F).
+ * Writes the row/column tile sizes, the wavefront grid of a workgroup
+ * (waves_m x waves_n), and the number of reduction slices; *mfma = 1 for
+ * the bf16 MFMA kernel, 0 for the float32-MFMA kernel.  Any output pointer
+ * may be NULL.
  */
 moe_status moe_grouped_gemm_plan(int product, int M, int K, int N, int E,
                                  moe_dtype dtype, int* tile_m, int* tile_n,
@@ -413,8 +414,9 @@ moe_status moe_act_bwd(const void* h, const void* da, int M, int F,
  * to dtype.  dh is bit for bit the result of moe_act_bwd.
  *   h, dh [M, 2F], da, a_scaled [M, F]: `dtype`.  row_scale float32 [M].
  */
-moe_status moe_act_bwd_scaled(const void* h, const void* da, const float* row_scale,
-                              int M, int F, moe_dtype dtype, void* dh, void* a_scaled,
+moe_status moe_act_bwd_scaled(const void* h, const void* da,
+                              const float* row_scale, int M, int F,
+                              moe_dtype dtype, void* dh, void* a_scaled,
                               moe_stream_t stream);
 
 #ifdef __cplusplus
