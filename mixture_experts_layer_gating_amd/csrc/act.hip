@@ -81,62 +81,54 @@ __global__ __launch_bounds__(kActBlock) void act_fwd_kernel(const T* __restrict_
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(kActBlock) void act_bwd_kernel(const T* __restrict__ h,
-                                                            const T* __restrict__ da, int M,
-                                                            int F, T* __restrict__ dh) {
-  constexpr int N = Elems<T>::N;
-  const int cpr = F / N;
-  const int total = M * cpr;
-  for (int i = blockIdx.x * kActBlock + threadIdx.x; i < total; i += gridDim.x * kActBlock) {
-    const int m = i / cpr, c = i - m * cpr;
-    const T* hr = h + static_cast<size_t>(m) * 2 * F + c * N;
-    float g[N], u[N], d[N], dg[N], du[N];
-    load_f32<true>(hr, g);  // h and da are not read again in the pass
-    load_f32<true>(hr + F, u);
-    load_f32<true>(da + static_cast<size_t>(m) * F + c * N, d);
-#pragma unroll
-    for (int e = 0; e < N; ++e) {
-      const float s = sigmoid_fast(g[e]);
-      dg[e] = d[e] * u[e] * s * (1.f + g[e] * (1.f - s));
-      du[e] = d[e] * g[e] * s;
-    }
-    T* dr = dh + static_cast<size_t>(m) * 2 * F + c * N;
-    store_f32(dr, dg);
-    store_f32(dr + F, du);
-  }
-}
-
-// act_bwd plus the activation itself, recomputed from h and scaled by a
-// per-row factor: a_s[m, :] = row_scale[m] * silu(G) * U, rounded once.  It
-// feeds GEMM 2's weight gradient when the combine's gradient is read through
-// the row map instead of being written (the gate weight moves from dc to a).
-template <typename T>
-__global__ __launch_bounds__(kActBlock) void act_bwd_scaled_kernel(
+// dh = [dG | dU] from h and da; with SCALED also the activation itself,
+// recomputed from h and scaled by a per-row factor: a_s[m, :] = row_scale[m]
+// * silu(G) * U, rounded once.  a_s feeds GEMM 2's weight gradient when the
+// combine's gradient is read through the row map instead of being written
+// (the gate weight moves from dc to a).  Each thread takes two chunks per
+// grid-stride step and issues both chunks' loads before using either (3%
+// faster than one chunk at T*k = 128 Ki rows, F = 1536).
+template <typename T, bool SCALED>
+__global__ __launch_bounds__(kActBlock) void act_bwd_kernel(
     const T* __restrict__ h, const T* __restrict__ da, const float* __restrict__ row_scale, int M,
     int F, T* __restrict__ dh, T* __restrict__ a_s) {
   constexpr int N = Elems<T>::N;
   const int cpr = F / N;
   const int total = M * cpr;
-  for (int i = blockIdx.x * kActBlock + threadIdx.x; i < total; i += gridDim.x * kActBlock) {
-    const int m = i / cpr, c = i - m * cpr;
-    const T* hr = h + static_cast<size_t>(m) * 2 * F + c * N;
-    float g[N], u[N], d[N], dg[N], du[N], o[N];
-    load_f32<true>(hr, g);
-    load_f32<true>(hr + F, u);
-    load_f32<true>(da + static_cast<size_t>(m) * F + c * N, d);
-    const float rs = row_scale[m];
+  const int stride = gridDim.x * kActBlock;
+  for (int i0 = blockIdx.x * kActBlock + threadIdx.x; i0 < total; i0 += 2 * stride) {
+    float g[2][N], u[2][N], d[2][N], rs[2];
+    int m[2], c[2];
+    bool live[2];
 #pragma unroll
-    for (int e = 0; e < N; ++e) {
-      const float s = sigmoid_fast(g[e]);
-      dg[e] = d[e] * u[e] * s * (1.f + g[e] * (1.f - s));
-      du[e] = d[e] * g[e] * s;
-      o[e] = rs * (g[e] * s * u[e]);
+    for (int r = 0; r < 2; ++r) {
+      // A chunk past the end repeats chunk i0's loads and is not stored.
+      const int i = i0 + r * stride;
+      live[r] = i < total;
+      m[r] = (live[r] ? i : i0) / cpr;
+      c[r] = (live[r] ? i : i0) - m[r] * cpr;
+      const T* hr = h + static_cast<size_t>(m[r]) * 2 * F + c[r] * N;
+      load_f32<true>(hr, g[r]);  // h and da are not read again in the pass
+      load_f32<true>(hr + F, u[r]);
+      load_f32<true>(da + static_cast<size_t>(m[r]) * F + c[r] * N, d[r]);
+      rs[r] = SCALED ? row_scale[m[r]] : 0.f;
     }
-    T* dr = dh + static_cast<size_t>(m) * 2 * F + c * N;
-    store_f32(dr, dg);
-    store_f32(dr + F, du);
-    store_f32(a_s + static_cast<size_t>(m) * F + c * N, o);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      if (!live[r]) continue;
+      float dg[N], du[N], o[N];
+#pragma unroll
+      for (int e = 0; e < N; ++e) {
+        const float s = sigmoid_fast(g[r][e]);
+        dg[e] = d[r][e] * u[r][e] * s * (1.f + g[r][e] * (1.f - s));
+        du[e] = d[r][e] * g[r][e] * s;
+        o[e] = rs[r] * (g[r][e] * s * u[r][e]);
+      }
+      T* dr = dh + static_cast<size_t>(m[r]) * 2 * F + c[r] * N;
+      store_f32(dr, dg);
+      store_f32(dr + F, du);
+      if constexpr (SCALED) store_f32(a_s + static_cast<size_t>(m[r]) * F + c[r] * N, o);
+    }
   }
 }
 
@@ -183,14 +175,15 @@ extern "C" moe_status moe_act_bwd(const void* h, const void* da, int M, int F, m
   clear_error();
   if (moe_status s = check_act(M, F, dtype)) return s;
   MOE_REQUIRE(h && da && dh, MOE_ERR_INVALID_ARG, "moe_act_bwd: null pointer");
+  const dim3 grid(act_grid(M, F, dtype)), block(kActBlock);
   if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(act_bwd_kernel<uint16_t>, dim3(act_grid(M, F, dtype)), dim3(kActBlock), 0,
-                       as_stream(stream), static_cast<const uint16_t*>(h),
-                       static_cast<const uint16_t*>(da), M, F, static_cast<uint16_t*>(dh));
+    hipLaunchKernelGGL((act_bwd_kernel<uint16_t, false>), grid, block, 0, as_stream(stream),
+                       static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(da), nullptr,
+                       M, F, static_cast<uint16_t*>(dh), nullptr);
   else
-    hipLaunchKernelGGL(act_bwd_kernel<float>, dim3(act_grid(M, F, dtype)), dim3(kActBlock), 0,
-                       as_stream(stream), static_cast<const float*>(h),
-                       static_cast<const float*>(da), M, F, static_cast<float*>(dh));
+    hipLaunchKernelGGL((act_bwd_kernel<float, false>), grid, block, 0, as_stream(stream),
+                       static_cast<const float*>(h), static_cast<const float*>(da), nullptr, M, F,
+                       static_cast<float*>(dh), nullptr);
   return check_launch("moe_act_bwd");
 }
 
@@ -203,12 +196,12 @@ extern "C" moe_status moe_act_bwd_scaled(const void* h, const void* da, const fl
               "moe_act_bwd_scaled: null pointer");
   const dim3 grid(act_grid(M, F, dtype)), block(kActBlock);
   if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(act_bwd_scaled_kernel<uint16_t>, grid, block, 0, as_stream(stream),
+    hipLaunchKernelGGL((act_bwd_kernel<uint16_t, true>), grid, block, 0, as_stream(stream),
                        static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(da),
                        row_scale, M, F, static_cast<uint16_t*>(dh),
                        static_cast<uint16_t*>(a_scaled));
   else
-    hipLaunchKernelGGL(act_bwd_scaled_kernel<float>, grid, block, 0, as_stream(stream),
+    hipLaunchKernelGGL((act_bwd_kernel<float, true>), grid, block, 0, as_stream(stream),
                        static_cast<const float*>(h), static_cast<const float*>(da), row_scale, M,
                        F, static_cast<float*>(dh), static_cast<float*>(a_scaled));
   return check_launch("moe_act_bwd_scaled");
