@@ -127,7 +127,9 @@ class MoELayer:
         if self.gather_dy:
             self.dyp = None
             self.w_sorted = torch.empty(Tk, dtype=f32, device=dev)
-            self.a_scaled = torch.empty(Tk, F, dtype=dtype, device=dev)
+            # The backward never reads `a` here, so the scaled activation
+            # takes its buffer (after backward(), `a` holds w * silu(g) * u).
+            self.a_scaled = self.a
         else:
             self.dyp = torch.empty(Tk, d, dtype=dtype, device=dev)
         self.dw = torch.empty(T, k, dtype=f32, device=dev)

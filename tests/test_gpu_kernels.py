@@ -351,6 +351,36 @@ def test_swiglu_bwd_scaled(M, F, dtype):
     assert rel(host(as1), ref) <= (TOL_ONE_ROUNDING if dtype == "bf16" else TOL_F32)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_swiglu_bwd_grid_stride(dtype):
+    """The backward kernels take two 16-byte chunks per thread per step of a
+    grid capped at 8192 workgroups: a size past two such steps, with a last
+    step whose second chunk (and, in fp32, more) lies past the end, against
+    the oracle (dh, and the scaled activation)."""
+    M, F = 37003, 1032  # bf16: 4.77 M chunks; fp32: 9.55 M; one step covers 4.19 M
+    say(f"swiglu bwd grid stride M={M} F={F} {dtype}")
+    tdt = DTYPES[dtype]
+    code = L.dtype_code(tdt)
+    h = _normal((M, 2 * F), 41, scale=3.0, dtype=dtype)
+    da = _normal((M, F), 42, dtype=dtype)
+    s = np.random.default_rng(43).random(M).astype(np.float32)
+    hd, dad = dev(h, tdt), dev(da, tdt)
+    dh0 = torch.empty(M, 2 * F, dtype=tdt, device=DEV)
+    L.moe_act_bwd(hd, dad, M, F, code, dh0)
+    dh1, as1 = torch.empty_like(dh0), torch.empty(M, F, dtype=tdt, device=DEV)
+    L.moe_act_bwd_scaled(hd, dad, dev(s), M, F, code, dh1, as1)
+    torch.cuda.synchronize()
+    tol = TOL_ONE_ROUNDING if dtype == "bf16" else TOL_F32
+    ref_dh = O.swiglu_backward(h, da)
+    assert rel(host(dh0), ref_dh) <= tol
+    assert rel(host(dh1), ref_dh) <= tol
+    # every row reached: the last rows on their own, not only in the norm
+    assert rel(host(dh0)[-3:], ref_dh[-3:]) <= tol
+    ref_as = O.swiglu(h) * s[:, None]
+    assert rel(host(as1), ref_as) <= tol
+    assert rel(host(as1)[-3:], ref_as[-3:]) <= tol
+
+
 SCALED_CASES = [(1024, 8, 256, 128, 16, "random"),   # 64x256 data-gradient tiles, 128x128 dW
                 (700, 3, 264, 136, 5, "empty"),      # ragged widths, an empty group
                 (4096, 2, 512, 256, 8, "skew"),      # 256x256 tiles
