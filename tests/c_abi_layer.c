@@ -3,17 +3,23 @@
  * no torch: it runs the MoE layer's forward pass -- router logits, top-k
  * softmax routing, counting and index generation, GEMM 1 with the SwiGLU
  * epilogue reading x through the row map, GEMM 2, the weighted combine --
- * on device buffers it allocates itself with the HIP runtime.
+ * and its backward pass (the combine's gradient read through the row map,
+ * as the Python layer does by default) on device buffers it allocates
+ * itself with the HIP runtime, on one stream.
  *
- *   c_abi_forward --check-host   host-only calls (version, validation errors,
- *                                workspace sizes, kernel plans); no GPU needed
- *   c_abi_forward IN OUT         forward pass on the inputs in IN, results
- *                                to OUT (formats below); exit 0 on success
+ *   c_abi_layer --check-host   host-only calls (version, validation errors,
+ *                              workspace sizes, kernel plans); no GPU needed
+ *   c_abi_layer IN OUT         forward and backward pass on the inputs in
+ *                              IN, results to OUT (formats below); exit 0
+ *                              on success
  *
  * IN  (little-endian): int32 magic 0x31454F4D, T, d, E, k, F; then bf16 bit
- *     patterns (uint16) of x [T, d], wr [d, E], W1 [E, d, 2F], W2 [E, F, d].
+ *     patterns (uint16) of x [T, d], wr [d, E], W1 [E, d, 2F], W2 [E, F, d],
+ *     dy [T, d].
  * OUT: logits float32 [T, E], topk_idx int32 [T, k], topk_w float32 [T, k],
- *      offsets int32 [E + 1], y bf16 bits [T, d], index-error mask uint32.
+ *      offsets int32 [E + 1], y bf16 bits [T, d], dx bf16 bits [T, d],
+ *      dWr float32 [d, E], dW1 float32 [E, d, 2F], dW2 float32 [E, F, d],
+ *      index-error mask uint32 (after the forward, then after the backward).
  */
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
@@ -98,17 +104,20 @@ int main(int argc, char** argv) {
   void* hwr = read_exact(in, (size_t)d * E * b2);
   void* hw1 = read_exact(in, (size_t)E * d * 2 * F * b2);
   void* hw2 = read_exact(in, (size_t)E * F * d * b2);
+  void* hdy = read_exact(in, (size_t)T * d * b2);
   fclose(in);
 
   void* x = to_device(hx, (size_t)T * d * b2);
   void* wr = to_device(hwr, (size_t)d * E * b2);
   void* w1 = to_device(hw1, (size_t)E * d * 2 * F * b2);
   void* w2 = to_device(hw2, (size_t)E * F * d * b2);
+  void* dy = to_device(hdy, (size_t)T * d * b2);
   const int32_t router_off_h[2] = {0, T};
   int32_t* router_off = (int32_t*)to_device(router_off_h, sizeof router_off_h);
   float* logits = (float*)to_device(NULL, (size_t)T * E * 4);
   int32_t* idx = (int32_t*)to_device(NULL, Tk * 4);
   float* w = (float*)to_device(NULL, Tk * 4);
+  float* probs = (float*)to_device(NULL, (size_t)T * E * 4);
   int32_t* counts = (int32_t*)to_device(NULL, (size_t)E * 4);
   int32_t* offsets = (int32_t*)to_device(NULL, (size_t)(E + 1) * 4);
   int32_t* dest = (int32_t*)to_device(NULL, Tk * 4);
@@ -119,14 +128,32 @@ int main(int argc, char** argv) {
   void* a = to_device(NULL, Tk * F * b2);
   void* yp = to_device(NULL, Tk * d * b2);
   void* y = to_device(NULL, (size_t)T * d * b2);
+  /* backward */
+  float* dw = (float*)to_device(NULL, Tk * 4);
+  float* w_sorted = (float*)to_device(NULL, Tk * 4);
+  void* da = to_device(NULL, Tk * F * b2);
+  void* dh = to_device(NULL, Tk * 2 * F * b2);
+  void* dxp = to_device(NULL, Tk * d * b2);
+  void* dx_e = to_device(NULL, (size_t)T * d * b2);
+  void* dx = to_device(NULL, (size_t)T * d * b2);
+  void* dlogits = to_device(NULL, (size_t)T * E * b2);
+  float* dwr = (float*)to_device(NULL, (size_t)d * E * 4);
+  float* dw1 = (float*)to_device(NULL, (size_t)E * d * 2 * F * 4);
+  float* dw2 = (float*)to_device(NULL, (size_t)E * F * d * 4);
+  size_t gws_bytes = moe_grouped_gemm_workspace_size(T, d, E, 1, MOE_BF16);
+  const size_t g2 = moe_grouped_gemm_workspace_size((int)Tk, F, d, E, MOE_BF16);
+  const size_t g1 = moe_grouped_gemm_workspace_size((int)Tk, d, 2 * F, E, MOE_BF16);
+  if (g2 > gws_bytes) gws_bytes = g2;
+  if (g1 > gws_bytes) gws_bytes = g1;
+  void* gws = to_device(NULL, gws_bytes);
 
-  unsigned int mask = 0;
+  unsigned int mask = 0, mask_bwd = 0;
   CHECK_MOE(moe_index_errors(&mask, 1, NULL)); /* start from a clear record */
 
   /* One stream (the null stream): every call only enqueues. */
   CHECK_MOE(moe_grouped_gemm_fwd(x, wr, router_off, T, d, E, 1, MOE_BF16, logits, MOE_F32,
                                  NULL, 0, NULL));
-  CHECK_MOE(moe_route_topk(logits, NULL, T, E, k, 0, NULL, idx, w, NULL, NULL));
+  CHECK_MOE(moe_route_topk(logits, NULL, T, E, k, 0, NULL, idx, w, probs, NULL));
   CHECK_MOE(moe_count_index(idx, T, k, E, counts, offsets, dest, src, ci_ws, ci_bytes, NULL));
   CHECK_MOE(moe_grouped_gemm_swiglu_fwd_gather(x, src, k, T, w1, offsets, (int)Tk, d, F, E,
                                                MOE_BF16, h, a, NULL));
@@ -136,6 +163,31 @@ int main(int argc, char** argv) {
   CHECK_HIP(hipDeviceSynchronize());
   CHECK_MOE(moe_index_errors(&mask, 1, NULL));
 
+  /* Backward of <y, dy>.  GEMM 2's backward reads dy through the row map
+   * with the gate weight as a row scale; the SwiGLU backward writes the
+   * scaled activation into a's buffer (a is not read again). */
+  CHECK_MOE(moe_unpermute_bwd(dy, yp, dest, w, T, k, d, MOE_BF16, NULL, dw, NULL));
+  CHECK_MOE(moe_gather_scale(w, src, (int)Tk, w_sorted, NULL));
+  CHECK_MOE(moe_grouped_gemm_bwd_scaled_gather(NULL, w2, dy, src, k, T, w_sorted, offsets,
+                                               (int)Tk, F, d, E, MOE_BF16, da, NULL, gws,
+                                               gws_bytes, NULL));
+  CHECK_MOE(moe_act_bwd_scaled(h, da, w_sorted, (int)Tk, F, MOE_BF16, dh, a, NULL));
+  CHECK_MOE(moe_grouped_gemm_bwd_scaled_gather(a, NULL, dy, src, k, T, w_sorted, offsets,
+                                               (int)Tk, F, d, E, MOE_BF16, NULL, dw2, gws,
+                                               gws_bytes, NULL));
+  CHECK_MOE(moe_grouped_gemm_bwd(NULL, w1, dh, offsets, (int)Tk, d, 2 * F, E, MOE_BF16, dxp,
+                                 NULL, NULL, gws, gws_bytes, NULL));
+  CHECK_MOE(moe_unpermute(dxp, dest, NULL, T, k, d, MOE_BF16, dx_e, NULL));
+  CHECK_MOE(moe_grouped_gemm_bwd_gather(x, src, k, T, w1, dh, offsets, (int)Tk, d, 2 * F, E,
+                                        MOE_BF16, NULL, NULL, dw1, gws, gws_bytes, NULL));
+  CHECK_MOE(moe_route_topk_bwd(probs, idx, dw, T, E, k, 0, dlogits, MOE_BF16, NULL));
+  CHECK_MOE(moe_grouped_gemm_bwd(x, wr, dlogits, router_off, T, d, E, 1, MOE_BF16, dx, dx_e,
+                                 NULL, gws, gws_bytes, NULL));
+  CHECK_MOE(moe_grouped_gemm_bwd(x, wr, dlogits, router_off, T, d, E, 1, MOE_BF16, NULL, NULL,
+                                 dwr, gws, gws_bytes, NULL));
+  CHECK_HIP(hipDeviceSynchronize());
+  CHECK_MOE(moe_index_errors(&mask_bwd, 1, NULL));
+
   FILE* out = fopen(argv[2], "wb");
   if (out == NULL) FAIL("cannot open %s", argv[2]);
   from_device(out, logits, (size_t)T * E * 4);
@@ -143,16 +195,23 @@ int main(int argc, char** argv) {
   from_device(out, w, Tk * 4);
   from_device(out, offsets, (size_t)(E + 1) * 4);
   from_device(out, y, (size_t)T * d * b2);
-  if (fwrite(&mask, sizeof mask, 1, out) != 1) FAIL("short write");
+  from_device(out, dx, (size_t)T * d * b2);
+  from_device(out, dwr, (size_t)d * E * 4);
+  from_device(out, dw1, (size_t)E * d * 2 * F * 4);
+  from_device(out, dw2, (size_t)E * F * d * 4);
+  if (fwrite(&mask, sizeof mask, 1, out) != 1 || fwrite(&mask_bwd, sizeof mask_bwd, 1, out) != 1)
+    FAIL("short write");
   fclose(out);
 
-  void* bufs[] = {x, wr, w1, w2, router_off, logits, idx, w, counts, offsets, dest, src,
-                  ci_ws, h, a, yp, y};
+  void* bufs[] = {x,  wr, w1,       w2, dy,  router_off, logits, idx, w,       probs, counts,
+                  offsets, dest, src, ci_ws, h, a, yp, y, dw, w_sorted, da, dh,
+                  dxp, dx_e, dx, dlogits, dwr, dw1, dw2, gws};
   for (size_t i = 0; i < sizeof bufs / sizeof bufs[0]; ++i) CHECK_HIP(hipFree(bufs[i]));
   free(hx);
   free(hwr);
   free(hw1);
   free(hw2);
-  printf("forward ok: T=%d d=%d E=%d k=%d F=%d\n", T, d, E, k, F);
+  free(hdy);
+  printf("forward and backward ok: T=%d d=%d E=%d k=%d F=%d\n", T, d, E, k, F);
   return 0;
 }

@@ -1,8 +1,8 @@
-"""The C ABI used from C: `tests/c_abi_forward.c` includes only
+"""The C ABI used from C: `tests/c_abi_layer.c` includes only
 `include/moe.h` and the HIP runtime header, is compiled here as C99 with
 warnings as errors, links the in-tree library, and runs the layer's forward
-pass on buffers it allocates itself.  Its results are held to the oracle
-like the Python-driven layer's."""
+and backward pass on buffers it allocates itself.  Its results are held to
+the oracle like the Python-driven layer's."""
 from __future__ import annotations
 
 import os
@@ -18,7 +18,7 @@ from moe_inputs import Workload, make_inputs
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PKG = os.path.join(ROOT, "mixture_experts_layer_gating_amd")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
-SRC = os.path.join(ROOT, "tests", "c_abi_forward.c")
+SRC = os.path.join(ROOT, "tests", "c_abi_layer.c")
 MAGIC = 0x31454F4D
 
 
@@ -28,7 +28,7 @@ def _compile(tmp_path):
         pytest.skip("no C compiler")
     if not os.path.exists(os.path.join(PKG, "libmoe.so")):
         pytest.fail("libmoe.so is not built (run __graft_entry__.build())")
-    exe = str(tmp_path / "c_abi_forward")
+    exe = str(tmp_path / "c_abi_layer")
     cmd = [cc, "-std=c99", "-O1", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROCM, "include"), SRC,
            "-L", PKG, "-lmoe", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
@@ -54,33 +54,36 @@ def test_c_consumer_host_calls(tmp_path):
 
 
 @pytest.mark.gpu
-def test_c_consumer_forward(tmp_path):
-    """Forward pass driven from C: logits to float32 accumulation accuracy
-    against the fp64 oracle; routing and offsets bit-exact against the
-    oracle's steps on the logits the C program got; y within the bf16
-    tolerance; no index-range event recorded."""
+def test_c_consumer_layer(tmp_path):
+    """Forward and backward pass driven from C: logits to float32
+    accumulation accuracy against the fp64 oracle; routing and offsets
+    bit-exact against the oracle's steps on the logits the C program got; y
+    and every gradient within the bf16 tolerance; no index-range event
+    recorded."""
     wl = Workload("c_abi", T=1000, d=256, E=16, k=4, F=136, dtype="bf16", w_std=0.05, seed=51)
     inp = make_inputs(wl)
     exe = _compile(tmp_path)
     fin, fout = tmp_path / "in.bin", tmp_path / "out.bin"
     with open(fin, "wb") as f:
         np.array([MAGIC, wl.T, wl.d, wl.E, wl.k, wl.F], dtype=np.int32).tofile(f)
-        for a in (inp.x, inp.wr, inp.w1, inp.w2):
+        for a in (inp.x, inp.wr, inp.w1, inp.w2, inp.dy):
             _bf16_bits(a).tofile(f)
-    print(f"c consumer forward {wl}", flush=True)
+    print(f"c consumer forward + backward {wl}", flush=True)
     p = subprocess.run([exe, str(fin), str(fout)], capture_output=True, text=True, timeout=180)
     assert p.returncode == 0, p.stdout + p.stderr
-    T, d, E, k = wl.T, wl.d, wl.E, wl.k
+    T, d, E, k, F = wl.T, wl.d, wl.E, wl.k, wl.F
     raw = open(fout, "rb").read()
     sizes = [("logits", np.float32, T * E), ("idx", np.int32, T * k), ("w", np.float32, T * k),
-             ("offsets", np.int32, E + 1), ("y", np.uint16, T * d), ("mask", np.uint32, 1)]
+             ("offsets", np.int32, E + 1), ("y", np.uint16, T * d), ("dx", np.uint16, T * d),
+             ("dwr", np.float32, d * E), ("dw1", np.float32, E * d * 2 * F),
+             ("dw2", np.float32, E * F * d), ("mask", np.uint32, 2)]
     got, pos = {}, 0
     for name, dt, n in sizes:
         nb = np.dtype(dt).itemsize * n
         got[name] = np.frombuffer(raw[pos:pos + nb], dtype=dt)
         pos += nb
     assert pos == len(raw)
-    assert int(got["mask"][0]) == 0
+    assert got["mask"].tolist() == [0, 0]
     logits = got["logits"].reshape(T, E).astype(np.float64)
     x, wr = (np.asarray(a, dtype=np.float64) for a in (inp.x, inp.wr))
     assert O.rel_fro(logits, x @ wr) <= 1e-5
@@ -88,5 +91,12 @@ def test_c_consumer_forward(tmp_path):
     np.testing.assert_array_equal(got["idx"], np.asarray(ref["idx"]).reshape(-1))
     np.testing.assert_array_equal(got["offsets"], np.asarray(ref["offsets"]).reshape(-1))
     assert O.rel_fro(got["w"].reshape(T, k), ref["w"]) <= 1e-5
-    y = (got["y"].astype(np.uint32) << 16).view(np.float32).reshape(T, d)
-    assert O.rel_fro(y, ref["y"]) <= 1e-2
+    def bf16(u):
+        return (u.astype(np.uint32) << 16).view(np.float32).reshape(T, d)
+
+    assert O.rel_fro(bf16(got["y"]), ref["y"]) <= 1e-2
+    bwd = O.layer_backward(ref, inp.dy, inp.x, inp.wr, inp.w1, inp.w2, k)
+    assert O.rel_fro(bf16(got["dx"]), bwd["dx"]) <= 1e-2
+    assert O.rel_fro(got["dwr"].reshape(d, E), bwd["dwr"]) <= 1e-2
+    assert O.rel_fro(got["dw1"].reshape(E, d, 2 * F), bwd["dw1"]) <= 1e-2
+    assert O.rel_fro(got["dw2"].reshape(E, F, d), bwd["dw2"]) <= 1e-2
