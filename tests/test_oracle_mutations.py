@@ -120,6 +120,65 @@ def permute_backward_first_slot_only(dxp, dest, k, T):
     return dxp[d2[:, 0]].copy()
 
 
+def biased_logits_ignores_bias(logits, bias):
+    return np.asarray(logits)
+
+
+def permute_slot_modulo(x, src, k):
+    # token of slot s taken as s % k (the slot's position j) instead of s // k
+    return np.asarray(x)[np.asarray(src) % k]
+
+
+def sigmoid_wrong_sign(z):
+    z = np.asarray(z, F64)
+    return 1.0 / (1.0 + np.exp(z))
+
+
+def count_tokens_shifted(idx, E):
+    flat = np.asarray(idx).reshape(-1)
+    return np.array([np.count_nonzero(flat == e + 1) for e in range(E)], dtype=np.int32)
+
+
+def grouped_matmul_drops_last_row(a, w, offsets):
+    a = np.asarray(a, F64)
+    E, K, N = w.shape
+    c = np.zeros((a.shape[0], N), dtype=F64)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1]) - 1
+        if r1 > r0:
+            c[r0:r1] = a[r0:r1] @ np.asarray(w[e], F64)
+    return c
+
+
+def combine_backward_unscaled(dy, yp, dest, w, k):
+    dyp, dw = OM._orig_combine_backward(dy, yp, dest, w, k)
+    T = np.asarray(dy).shape[0]
+    d2 = np.asarray(dest).reshape(T, k)
+    for j in range(k):
+        dyp[d2[:, j]] = np.asarray(dy, F64)  # the gate weight left out
+    return dyp, dw
+
+
+def combine_backward_wrong_slot(dy, yp, dest, w, k):
+    dyp, dw = OM._orig_combine_backward(dy, yp, dest, w, k)
+    dy = np.asarray(dy, F64)
+    yp = np.asarray(yp, F64)
+    T = dy.shape[0]
+    d2 = np.asarray(dest).reshape(T, k)
+    for j in range(k):  # dw of slot j from the row of slot j + 1
+        dw[:, j] = np.sum(dy * yp[d2[:, (j + 1) % k]], axis=1)
+    return dyp, dw
+
+
+def gate_backward_renorm_term_dropped(p, idx, dw, renorm=False):
+    if not renorm:
+        return OM._orig_gate_backward(p, idx, dw)
+    p = np.asarray(p, F64)
+    idx = np.asarray(idx, np.int64)
+    S = np.take_along_axis(p, idx, axis=1).sum(axis=1, keepdims=True)
+    return OM._orig_gate_backward(p, idx, np.asarray(dw, F64) / S)
+
+
 # ----------------------------------------------------------------- pins to run
 FD = [lambda: P.test_backward_matches_central_differences(False, False, False),
       lambda: P.test_backward_matches_central_differences(True, False, False),
@@ -155,6 +214,26 @@ CASES = {
                                                grouped_matmul_backward_no_transpose, FD),
     "router backward drops dx": ("router_backward", router_backward_no_dx, FD),
     "permute backward sums one slot": ("permute_backward", permute_backward_first_slot_only, FD),
+    "bias left out of the selection scores": ("biased_logits", biased_logits_ignores_bias,
+                                              [P.test_route_bias_and_forced,
+                                               P.test_biased_logits_add_in_logit_precision]),
+    "permute takes the slot's position as its token": ("permute", permute_slot_modulo,
+                                                       [P.test_permute_groups_hold_the_routed_tokens]
+                                                       + DENSE),
+    "sigmoid with the wrong sign": ("sigmoid", sigmoid_wrong_sign, [P.test_silu_closed_forms]),
+    "counts shifted by one expert": ("count_tokens", count_tokens_shifted,
+                                     [lambda: P.test_counts_and_index_against_library_and_brute_force(64, 8, 64),
+                                      P.test_index_hand_example]),
+    "grouped matmul drops each group's last row": ("grouped_matmul", grouped_matmul_drops_last_row,
+                                                   [P.test_grouped_matmul_brute_force] + DENSE),
+    "combine backward leaves out the gate weight": ("combine_backward", combine_backward_unscaled,
+                                                    FD),
+    "combine backward reads the wrong slot's row": ("combine_backward",
+                                                    combine_backward_wrong_slot, FD),
+    "gate backward drops the renormalisation term": ("gate_backward",
+                                                     gate_backward_renorm_term_dropped,
+                                                     [P.test_gate_backward_matches_central_differences]
+                                                     + FD),
 }
 
 
@@ -166,9 +245,11 @@ def _plant(monkeypatch, name, fn):
 
 
 def _fails(pin):
+    # A pin fails by an assertion, or by an error the mutant provokes (a
+    # count that no longer matches the rows, say): either way it does not pass.
     try:
         pin()
-    except AssertionError:
+    except Exception:  # noqa: BLE001
         return True
     return False
 
